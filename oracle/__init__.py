@@ -1,0 +1,185 @@
+"""CPU oracle for paged attention -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, double-precision model of the paged-attention path (see
+pa_oracle.c for the passages each function follows). Only tests/,
+__graft_entry__.smoke() and bench.py's cpu_baseline leg may import this
+package. It shares no code with the HIP library (paged_kv_cache_109_amd) and
+never imports it; the product path never imports this.
+
+The C source is compiled with gcc (no fast-math) into oracle/_build/.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+_BUILD = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_BUILD, "libpaoracle.so")
+_DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+_ERRORS = {
+    -1: "block table entry outside the pool",
+    -2: "slot outside the pool",
+    -3: "duplicate slot",
+    -4: "bad copy mapping (out of range, repeated destination, or destination is a source)",
+    -5: "bad argument",
+    -6: "out of memory",
+}
+_lib = None
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle with gcc -O2 -fopenmp into a shared library."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Werror",
+               src, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def _bind(lib):
+    P = ctypes.c_void_p
+    i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    lib.oracle_to_f64.argtypes = [P, P, i64, ctypes.c_int]
+    lib.oracle_to_f64.restype = ctypes.c_int
+    lib.oracle_slot.argtypes = [P, i64, i32]
+    lib.oracle_slot.restype = i64
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_decode.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, i32, i64, f64, i32, i32]
+    lib.oracle_decode.restype = ctypes.c_int
+    lib.oracle_prefill_chunk.argtypes = [P, P, P, P, P, P, i32, P, i32, i32, i32, i32, i64, f64, i32, i32]
+    lib.oracle_prefill_chunk.restype = ctypes.c_int
+    lib.oracle_reshape_and_cache.argtypes = [P, P, P, P, i64, i64, P, i64, i32, i32, i32, i64, i32]
+    lib.oracle_reshape_and_cache.restype = ctypes.c_int
+    lib.oracle_copy_blocks.argtypes = [P, P, i32, P, i64, i64, i64]
+    lib.oracle_copy_blocks.restype = ctypes.c_int
+    return lib
+
+
+def load(path: Optional[str] = None):
+    """Load the oracle library (building it first if it is not built)."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise OracleError(_ERRORS.get(rc, f"error {rc}"))
+
+
+def _c(a, dtype=None) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def max_threads(lib=None) -> int:
+    return int((lib or load()).oracle_max_threads())
+
+
+def to_f64(arr: np.ndarray, dtype: str, lib=None) -> np.ndarray:
+    """Widen storage elements (f32, f16, or bf16 bit patterns) to float64."""
+    a = _c(arr)
+    out = np.empty(a.size, dtype=np.float64)
+    _check((lib or load()).oracle_to_f64(_ptr(out), _ptr(a), a.size, _DTYPE_CODE[dtype]))
+    return out.reshape(a.shape)
+
+
+def slot(table_row: Sequence[int], position: int, block_size: int, lib=None) -> int:
+    """Flat cache slot (physical block * B + offset) of a logical position."""
+    t = _c(table_row, np.int32)
+    return int((lib or load()).oracle_slot(_ptr(t), int(position), int(block_size)))
+
+
+def slots(block_tables: np.ndarray, seq: np.ndarray, pos: np.ndarray, block_size: int, lib=None) -> np.ndarray:
+    """Slot of each (seq[t], pos[t]) token; the oracle's own translation."""
+    bt = _c(block_tables, np.int32)
+    lib = lib or load()
+    out = np.empty(len(seq), dtype=np.int64)
+    for i, (s, p) in enumerate(zip(seq, pos)):
+        out[i] = lib.oracle_slot(bt[int(s)].ctypes.data, int(p), int(block_size))
+    return out
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, dtype: str,
+           threads: int = 0, lib=None) -> np.ndarray:
+    """Paged decode attention; returns float64 [num_seqs, num_heads, head_dim]."""
+    q, k, v = _c(q), _c(k_cache), _c(v_cache)
+    bt, ctx = _c(block_tables, np.int32), _c(context_lens, np.int32)
+    S, H, D = q.shape
+    N, Hk, B, Dk = k.shape
+    assert (Hk, Dk) == (H, D) and v.shape == k.shape and bt.shape[0] == S == ctx.shape[0]
+    out = np.empty((S, H, D), dtype=np.float64)
+    _check((lib or load()).oracle_decode(
+        _ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(bt), bt.shape[1], _ptr(ctx), S, H, D, B, N,
+        float(scale), _DTYPE_CODE[dtype], int(threads)))
+    return out
+
+
+def prefill_chunk(q, cu_q_lens, k_cache, v_cache, block_tables, context_lens, scale: float,
+                  dtype: str, threads: int = 0, lib=None) -> np.ndarray:
+    """Causal chunk attention over a paged cache; float64 [total_q, H, D]."""
+    q, k, v = _c(q), _c(k_cache), _c(v_cache)
+    cu = _c(cu_q_lens, np.int32)
+    bt, ctx = _c(block_tables, np.int32), _c(context_lens, np.int32)
+    T, H, D = q.shape
+    N, Hk, B, Dk = k.shape
+    S = ctx.shape[0]
+    assert (Hk, Dk) == (H, D) and cu.shape == (S + 1,) and int(cu[-1]) == T
+    out = np.empty((T, H, D), dtype=np.float64)
+    _check((lib or load()).oracle_prefill_chunk(
+        _ptr(out), _ptr(q), _ptr(cu), _ptr(k), _ptr(v), _ptr(bt), bt.shape[1], _ptr(ctx), S, H, D,
+        B, N, float(scale), _DTYPE_CODE[dtype], int(threads)))
+    return out
+
+
+def reshape_and_cache(k_cache: np.ndarray, v_cache: np.ndarray, key, value, slot_mapping,
+                      dtype: str, lib=None) -> None:
+    """Write new K/V rows into the caches in place (raw byte copies)."""
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    key, value = _c(key), _c(value)
+    sm = _c(slot_mapping, np.int64)
+    N, H, B, D = k_cache.shape
+    T = sm.shape[0]
+    assert key.shape == (T, H, D) and value.shape == (T, H, D)
+    _check((lib or load()).oracle_reshape_and_cache(
+        _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value), H * D, H * D, _ptr(sm), T, H, D, B,
+        N, _DTYPE_CODE[dtype]))
+
+
+def copy_blocks(k_caches: Sequence[np.ndarray], v_caches: Sequence[np.ndarray], block_mapping,
+                lib=None) -> None:
+    """Copy whole blocks src -> dst in every layer's K and V cache, in place."""
+    L = len(k_caches)
+    assert len(v_caches) == L and L > 0
+    for a in list(k_caches) + list(v_caches):
+        assert a.flags.c_contiguous and a.shape == k_caches[0].shape
+    bm = _c(block_mapping, np.int64).reshape(-1, 2)
+    N = k_caches[0].shape[0]
+    block_bytes = k_caches[0].nbytes // N
+    kp = (ctypes.c_void_p * L)(*[a.ctypes.data for a in k_caches])
+    vp = (ctypes.c_void_p * L)(*[a.ctypes.data for a in v_caches])
+    _check((lib or load()).oracle_copy_blocks(
+        ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp, ctypes.c_void_p), L, _ptr(bm),
+        bm.shape[0], block_bytes, N))
