@@ -1,0 +1,207 @@
+"""Benchmark of the paged decode-attention step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload opt13b_b64]
+
+A step is one decode iteration of the hot path over one batch (the loop the
+Korean review of the vLLM paper, mz-moonzoo.tistory.com/116, section 4.3,
+describes): write each sequence's new K/V into its cache slot
+(reshape_and_cache), then attend with one query per sequence over the paged
+cache (decode partition pass + reduce pass). Inputs are seeded synthetic
+tensors of the workload's shapes, resident in HBM before timing starts.
+
+Prints ONE JSON line. `value` is decode tokens/s for one layer call (one
+query token per sequence per step). `roofline` is for the dominant kernel,
+the decode partition pass, whose launches are bracketed by HIP events on the
+stream they run on. `cpu_baseline` times the CPU oracle (test
+infrastructure, never tuned) on the same batch on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+METRIC = "paged decode attn tokens/s + effective KV GB/s (% HBM peak), OPT-13B shapes"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="opt13b_b64", choices=["opt13b_b64", "large_batch_b256"])
+    ap.add_argument("--replicas", type=int, default=2,
+                    help="copies of the KV pool used in turn, so no step finds the last one's data in cache")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-runs", type=int, default=3)
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    src = open(os.path.join(ROOT, "paged_kv_cache_109_amd", "csrc", "pa_decode.hip"), "rb").read()
+    return hashlib.sha256(src).hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per partition-kernel launch from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"decode_partition_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_source_digest():
+        return None
+    return float(t.group(1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this library has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_109_amd as pa
+    import workloads as W
+
+    t0 = time.time()
+    case = {"opt13b_b64": W.opt13b_b64, "large_batch_b256": W.large_batch_b256}[args.workload]()
+    print(f"[bench] workload {case.name} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
+
+    def to_dev(a, dtype=None):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if case.dtype == "bf16" and dtype == "bf16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.to(dev)
+
+    S, H, D, B = case.num_seqs, case.num_heads, case.head_dim, case.block_size
+    q = to_dev(case.q, case.dtype)
+    pools = [(to_dev(case.k_cache, case.dtype), to_dev(case.v_cache, case.dtype)) for _ in range(args.replicas)]
+    block_tables = to_dev(case.block_tables)
+    context_lens = to_dev(case.context_lens)
+    slots = to_dev(pa.slot_mapping(case.block_tables, case.new_seq, case.new_pos, B))
+    new_k, new_v = to_dev(case.new_key, case.dtype), to_dev(case.new_value, case.dtype)
+    out = torch.empty_like(q)
+    max_ctx = case.max_context_len
+    part = args.partition_size
+    ws = pa.alloc_decode_workspace(S, H, D, max_ctx, B, part, device=dev)
+    stream = torch.cuda.current_stream()
+
+    # Calibration kernel for the HBM byte counters: a plain 1 GiB copy.
+    cal_src = torch.empty(1 << 29, dtype=torch.float16, device=dev).fill_(1.0)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    # Streaming-read reference on this machine: sum of a 4 GiB tensor.
+    big = torch.ones(1 << 31, dtype=torch.float16, device=dev)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    big.sum()
+    e0.record(); big.sum(); e1.record(); torch.cuda.synchronize()
+    stream_read_gbps = big.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del big, cal_src, cal_dst
+    torch.cuda.empty_cache()
+
+    def step(i, ev=None):
+        k_cache, v_cache = pools[i % len(pools)]
+        pa.reshape_and_cache(new_k, new_v, k_cache, v_cache, slots)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.paged_attention_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, max_ctx,
+                                             case.scale, workspace=ws, partition_size=part)
+        if ev is not None:
+            ev[1].record(stream)
+        pa.paged_attention_decode_reduce(out, context_lens, max_ctx, case.max_blocks_per_seq, H, D, B,
+                                         workspace=ws, partition_size=part)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    part_ms = [a.elapsed_time(b) for a, b in evs]
+    part_avg_s = float(np.mean(part_ms)) * 1e-3
+    print(f"[bench] step {ms_per_step * 1e3:.1f} us; partition kernel avg {part_avg_s * 1e6:.1f} us "
+          f"(min {min(part_ms) * 1e3:.1f}, max {max(part_ms) * 1e3:.1f})", file=sys.stderr, flush=True)
+
+    elt = case.elt_bytes
+    kv_bytes = W.logical_kv_bytes(case.context_lens, H, D, elt)
+    nblocks = int(sum(W.blocks_needed(n, B) for n in case.context_lens))
+    # Algorithmic bytes of one partition-pass launch: every valid token's K and
+    # V row once, q in, the output out, the table entries and lengths.
+    alg_bytes = kv_bytes + 2 * S * H * D * elt + 4 * nblocks + 4 * S
+    achieved = alg_bytes / part_avg_s / 1e9
+    tokens_per_s = S / (ms_per_step * 1e-3)
+    traffic = committed_traffic(case.name.rsplit("_", 1)[0])
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.load()
+        threads = len(os.sched_getaffinity(0))
+        times = []
+        for _ in range(args.cpu_runs):
+            t = time.perf_counter()
+            oracle.decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens, case.scale,
+                          case.dtype, threads=threads)
+            times.append(time.perf_counter() - t)
+        t_med = float(np.median(times))
+        cpu = {"value": S / t_med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"the whole {case.name} batch ({S} seqs, {int(case.context_lens.sum())} context tokens, "
+                         f"{H} heads) decoded {args.cpu_runs} times by the fp64 C oracle with OpenMP over "
+                         f"(seq, head); median {t_med:.2f}s; CPU {platform.processor() or platform.machine()}",
+               "effective_kv_gbps": kv_bytes / t_med / 1e9}
+
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": {"workload": case.name, "num_seqs": S, "num_heads": H, "head_dim": D, "block_size": B,
+                   "context_tokens": int(case.context_lens.sum()), "max_context_len": max_ctx,
+                   "partition_size": part or pa.decode_partition_size(max_ctx, B), "pool_replicas": args.replicas,
+                   "step": "reshape_and_cache(new tokens) + decode partitions + decode reduce"},
+        "effective_kv_gbps": kv_bytes / (ms_per_step * 1e-3) / 1e9,
+        "pct_hbm_peak": kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "measured_stream_read_gbps": stream_read_gbps,
+        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "alg_bytes_per_launch": alg_bytes, "avg_launch_us": part_avg_s * 1e6},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

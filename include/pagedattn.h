@@ -1,0 +1,230 @@
+/*
+ * pagedattn.h -- C ABI of libpagedattn: attention over a paged KV cache on
+ * AMD Instinct MI355X (gfx950, CDNA4), with the cache write and block copy
+ * that go with it.
+ *
+ * The method: a sequence's keys and values live in fixed-size blocks of
+ * block_size tokens that need not be adjacent in memory; a per-sequence block
+ * table maps logical block i (positions i*B .. i*B+B-1) to a physical block.
+ * Attention of a query over the sequence is ordinary softmax attention over
+ * exactly its context_len valid positions, computed by visiting the blocks
+ * where they lie (paper notes "PagedAttention: Efficient Memory Management for
+ * Large Language Model Serving with PagedAttention", unpurerationalist.github.io,
+ * section 3.1 and its block-wise attention equation; Korean review
+ * mz-moonzoo.tistory.com/116, section 4.1).  The three fused kernels of that
+ * design -- block write, block read + attention, batched block copy -- are the
+ * entry points below (review section 5.1; notes section 4.1).
+ *
+ * Conventions for every call
+ *  - All data pointers are DEVICE pointers allocated by the caller (e.g. by
+ *    PyTorch); the library keeps no pointer after a call returns, allocates
+ *    nothing, and holds no mutable global state: calls are re-entrant.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on that stream and returns without synchronising.
+ *  - Layouts are C-contiguous:
+ *      caches      [num_blocks][num_heads][block_size][head_dim]
+ *      q, out      [rows][num_heads][head_dim]
+ *      block_tables[num_seqs][max_blocks_per_seq]   int32
+ *      context_lens[num_seqs]                       int32
+ *  - Positions, logical blocks and slots count from 0.  The flat slot of
+ *    position p of a sequence is block_tables[s][p / B] * B + p % B
+ *    ("KV 캐시 관리와 PagedAttention", llm-systems-engineering.pages.dev,
+ *    section on linking token order to storage).
+ *  - Supported shapes: head_dim 64 or 128; block_size 4, 8, 16 or 32; dtype
+ *    fp32, fp16 or bf16 (the prefill chunk: fp16/bf16, head_dim 128).  All
+ *    data pointers must be 16-byte aligned.
+ *  - Errors are found by synchronous host checks on the scalar arguments and
+ *    pointers (never on device data).  On any error the call returns a
+ *    non-zero status, enqueues nothing and writes nothing; pa_last_error()
+ *    then describes the problem.  PA_ERR_HIP means a launch failed.
+ *  - Data-dependent preconditions cannot be checked without a device sync and
+ *    are the caller's: table entries of valid positions in [0, num_blocks);
+ *    context_lens[s] <= max_context_len <= max_blocks_per_seq * block_size;
+ *    slots of one reshape call distinct; copy destinations distinct and not
+ *    sources.  The kernels never read or write outside the buffers whatever
+ *    the device data holds: a table entry outside [0, num_blocks) makes its
+ *    block contribute nothing; a slot outside the pool is skipped; a copy
+ *    pair outside the pool is skipped; context lengths are clipped to
+ *    [0, min(max_context_len, max_blocks_per_seq * block_size)].
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, misalignment, inconsistent sizes */
+  PA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, block_size or dtype */
+  PA_ERR_WORKSPACE = 3,   /* decode workspace missing or too small */
+  PA_ERR_HIP = 4          /* a kernel launch failed */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* PA_ABI_VERSION of the built library. */
+int pa_abi_version(void);
+
+/* Static text for a status code. */
+const char *pa_status_string(pa_status status);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char *pa_last_error(void);
+
+/*
+ * pa_reshape_and_cache -- write new K/V rows into their cache slots.
+ *
+ * The fused reshape-and-block-write kernel (review section 5.1, item 1; notes
+ * section 4.1): for every token t with slot = slot_mapping[t] >= 0 and every
+ * head h, the head_dim elements key[t][h][:] are copied bit for bit into
+ * k_cache[slot / B][h][slot % B][:], and value[t][h][:] into v_cache
+ * likewise.  Nothing else is written.  A negative slot means "no write" (a
+ * padding token).
+ *
+ *  key, value         device [num_tokens][num_heads][head_dim]; consecutive
+ *                     tokens are key_token_stride / value_token_stride
+ *                     ELEMENTS apart (>= num_heads*head_dim, and a multiple of
+ *                     16 bytes), heads are contiguous within a token, so a
+ *                     slice of a fused QKV tensor can be passed directly.
+ *  k_cache, v_cache   device caches, num_blocks blocks.
+ *  slot_mapping       device int64 [num_tokens].
+ *  num_tokens         >= 0 (0 is a no-op).
+ */
+pa_status pa_reshape_and_cache(const void *key, const void *value, int64_t key_token_stride,
+                               int64_t value_token_stride, void *k_cache, void *v_cache,
+                               const int64_t *slot_mapping, int64_t num_tokens, int32_t num_heads,
+                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                               pa_dtype dtype, void *stream);
+
+/*
+ * Decode attention is split into a partition pass and a reduce pass.  The
+ * context of a sequence is cut into partitions of partition_size tokens;
+ * each partition is attended independently (the block-separability of the
+ * attention sum, review section 4.1) and the partial results -- running max
+ * m, running sum l and the unnormalised weighted value sum -- are merged by
+ * the reduce pass.  When max_context_len <= partition_size no workspace is
+ * needed and the partition pass writes the output itself.
+ *
+ * partition_size: 0 lets the library choose (pa_decode_partition_size);
+ * otherwise a positive multiple of 16 and of block_size.
+ */
+int32_t pa_decode_partition_size(int32_t max_context_len, int32_t block_size);
+
+/* Workspace bytes pa_paged_attention_decode needs (0 when one partition
+ * covers max_context_len).  Layout: fp32 (m, l) pairs
+ * [num_seqs][num_heads][P_max] followed by fp32 partial sums
+ * [num_seqs][num_heads][P_max][head_dim], P_max = ceil(max_context_len /
+ * partition_size).  Its contents need no initialisation. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t block_size,
+                                 int32_t partition_size);
+
+/*
+ * pa_paged_attention_decode -- one query per sequence over its paged KV.
+ *
+ * For each sequence s (n = context_lens[s], which counts the current token,
+ * written beforehand by pa_reshape_and_cache: "KV 캐시 관리와 PagedAttention",
+ * section on attention over scattered KV) and head h:
+ *     out[s][h][:] = sum_p softmax_p(scale * q[s][h][:] . k_p) * v_p
+ * over positions p = 0..n-1, k_p / v_p read from the physical block
+ * block_tables[s][p / B] at offset p % B.  n = 0 gives a zero output.
+ * Arithmetic: inputs in `dtype`, products, sums and softmax in fp32, the
+ * output rounded to `dtype` (nearest even).
+ *
+ *  out              device [num_seqs][num_heads][head_dim], `dtype`.
+ *  q                device [num_seqs][num_heads][head_dim], `dtype`.
+ *  max_context_len  host upper bound of context_lens (sizes the grid).
+ *  scale            softmax scale, normally 1/sqrt(head_dim).
+ *  workspace        device, >= pa_decode_workspace_bytes(...) bytes, 16-byte
+ *                   aligned; may be NULL when that size is 0.
+ */
+pa_status pa_paged_attention_decode(void *out, const void *q, const void *k_cache,
+                                    const void *v_cache, const int32_t *block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                    int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                                    int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                    float scale, pa_dtype dtype, int32_t partition_size,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* The partition pass alone (same arguments).  Writes `out` for sequences with
+ * at most one partition and the workspace for the others. */
+pa_status pa_paged_attention_decode_partitions(
+    void *out, const void *q, const void *k_cache, const void *v_cache, const int32_t *block_tables,
+    int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+    int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+    float scale, pa_dtype dtype, int32_t partition_size, void *workspace, size_t workspace_bytes,
+    void *stream);
+
+/* The reduce pass alone: merges the partials of sequences with two or more
+ * partitions into `out`.  A no-op when max_context_len <= partition_size.
+ * Arguments as for pa_paged_attention_decode (same partition_size). */
+pa_status pa_paged_attention_decode_reduce(void *out, const int32_t *context_lens,
+                                           int32_t max_context_len, int32_t max_blocks_per_seq,
+                                           int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                           int32_t block_size, pa_dtype dtype,
+                                           int32_t partition_size, const void *workspace,
+                                           size_t workspace_bytes, void *stream);
+
+/*
+ * pa_copy_blocks -- batched whole-block copy for copy-on-write.
+ *
+ * The fused block-copy kernel (review section 5.1, item 3; notes section
+ * 4.1): one launch copies, for every layer l < num_layers and every pair
+ * (src, dst) = (block_mapping[2i], block_mapping[2i+1]), the block_bytes
+ * bytes of physical block src onto block dst, in k_caches[l] and in
+ * v_caches[l] -- every head and every slot, filled or not ("KV 캐시 관리와
+ * PagedAttention", copy-on-write section: the copy keeps the K/V already in
+ * the block).
+ *
+ *  k_caches, v_caches  HOST arrays of num_layers DEVICE pointers; each cache
+ *                      holds num_blocks blocks of block_bytes bytes.  The
+ *                      host arrays are read during the call only.
+ *  block_mapping       DEVICE int64 [num_pairs][2].
+ *  block_bytes         num_heads*block_size*head_dim*element size; a
+ *                      positive multiple of 16.
+ *  num_pairs           >= 0 (0 is a no-op); num_layers >= 1.
+ */
+pa_status pa_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t num_layers,
+                         const int64_t *block_mapping, int64_t num_pairs, int64_t block_bytes,
+                         int64_t num_blocks, void *stream);
+
+/*
+ * pa_paged_attention_prefill_chunk -- causal attention of a chunk of queries
+ * over a paged cache (chunked prefill; teardown of vLLM's scheduler on
+ * arcyou.ai, continuous-batching section, where long prompts are split into
+ * chunks).  The chunk's own K/V must already be in the cache
+ * (pa_reshape_and_cache).
+ *
+ * Sequence s owns query rows cu_q_lens[s] .. cu_q_lens[s+1]-1 (q_len rows);
+ * context_lens[s] counts its cached tokens plus the chunk, so the chunk
+ * starts at c = context_lens[s] - q_len and query j attends, with the same
+ * softmax as decode, to positions 0 .. c+j.
+ *
+ *  out, q          device [total_q][num_heads][head_dim], fp16 or bf16.
+ *  cu_q_lens       device int32 [num_seqs + 1], non-decreasing, from 0 to
+ *                  total_q.
+ *  max_q_len       host bound of the per-sequence q_len.
+ *  max_context_len host bound of context_lens.
+ */
+pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32_t *cu_q_lens,
+                                           const void *k_cache, const void *v_cache,
+                                           const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t *context_lens, int32_t num_seqs,
+                                           int32_t total_q, int32_t max_q_len,
+                                           int32_t max_context_len, int32_t num_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int64_t num_blocks, float scale, pa_dtype dtype,
+                                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

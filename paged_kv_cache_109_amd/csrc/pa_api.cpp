@@ -1,0 +1,367 @@
+// C-ABI entry points of libpagedattn: argument checks, partition sizing and
+// dispatch to the kernel launchers.  Every check here is on host scalars and
+// pointer values; device data is never read.  On any failed check nothing is
+// enqueued.
+#include "../../include/pagedattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pa_status ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+pa_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(PA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elt_bytes(pa_dtype dt) { return dt == PA_F32 ? 4 : 2; }
+
+bool valid_dtype(int dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Default tokens per decode partition: 512 tokens (32 blocks of 16), kept a
+// multiple of 16 and of B and within one table entry per lane.
+int32_t default_partition(int32_t block_size) {
+  int64_t p = 512;
+  if (p > (int64_t)pa::kMaxPartitionBlocks * block_size) p = (int64_t)pa::kMaxPartitionBlocks * block_size;
+  return (int32_t)p;
+}
+
+pa_status check_partition(int32_t partition_size, int32_t block_size) {
+  if (partition_size <= 0 || partition_size % pa::kDecodeTile != 0 || partition_size % block_size != 0)
+    return fail(PA_ERR_INVALID_ARG, "partition_size %d must be a positive multiple of %d and of block_size %d",
+                partition_size, pa::kDecodeTile, block_size);
+  if ((int64_t)partition_size > (int64_t)pa::kMaxPartitionBlocks * block_size)
+    return fail(PA_ERR_INVALID_ARG, "partition_size %d spans more than %d blocks of %d", partition_size,
+                pa::kMaxPartitionBlocks, block_size);
+  return PA_OK;
+}
+
+struct DecodeGeometry {
+  int32_t ctx_cap;
+  int32_t part_tokens;
+  int32_t max_parts;
+  size_t ws_bytes;
+};
+
+DecodeGeometry geometry(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
+                        int32_t max_blocks, int32_t block_size, int32_t partition_size) {
+  DecodeGeometry g;
+  int64_t cap = max_context_len;
+  if (max_blocks >= 0 && (int64_t)max_blocks * block_size < cap) cap = (int64_t)max_blocks * block_size;
+  g.ctx_cap = (int32_t)(cap < 0 ? 0 : cap);
+  g.part_tokens = partition_size > 0 ? partition_size : default_partition(block_size);
+  g.max_parts = (int32_t)ceil_div(g.ctx_cap > 0 ? g.ctx_cap : 1, g.part_tokens);
+  if (g.max_parts <= 1) {
+    g.ws_bytes = 0;
+  } else {
+    const size_t rows = (size_t)num_seqs * num_heads * g.max_parts;
+    g.ws_bytes = rows * 2 * sizeof(float) + rows * (size_t)head_dim * sizeof(float);
+  }
+  return g;
+}
+
+pa_status check_decode_common(const void *k_cache, const void *v_cache, const int32_t *block_tables,
+                              int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+                              int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                              int64_t num_blocks, pa_dtype dtype, int32_t partition_size) {
+  if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "dtype %d is not one of PA_F32/PA_F16/PA_BF16", dtype);
+  if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_context_len < 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "sizes must be positive (num_seqs >= 0, max_context_len >= 0): num_seqs=%d num_heads=%d "
+                "head_dim=%d block_size=%d num_blocks=%lld max_blocks_per_seq=%d max_context_len=%d",
+                num_seqs, num_heads, head_dim, block_size, (long long)num_blocks, max_blocks_per_seq,
+                max_context_len);
+  if (!pa::decode_supported(dtype, head_dim, block_size))
+    return fail(PA_ERR_UNSUPPORTED, "decode is built for head_dim 64/128 and block_size 4/8/16/32 (got %d, %d)",
+                head_dim, block_size);
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs %d exceeds 65535", num_seqs);
+  if (num_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "num_heads %d exceeds 65535", num_heads);
+  if (num_seqs > 0 && (!k_cache || !v_cache || !block_tables || !context_lens))
+    return fail(PA_ERR_INVALID_ARG, "null cache, block table or context-length pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return fail(PA_ERR_INVALID_ARG, "caches must be 16-byte aligned");
+  if (partition_size != 0) {
+    pa_status st = check_partition(partition_size, block_size);
+    if (st != PA_OK) return st;
+  }
+  (void)elt_bytes(dtype);
+  return PA_OK;
+}
+
+pa::DecodeArgs decode_args(void *out, const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                           int32_t num_seqs, int32_t num_heads, int64_t num_blocks, float scale,
+                           const DecodeGeometry &g, const void *workspace) {
+  pa::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_heads = num_heads;
+  a.ctx_cap = g.ctx_cap;
+  a.part_tokens = g.part_tokens;
+  a.max_parts = g.max_parts;
+  a.scale_log2 = scale * kLog2e;
+  const size_t rows = (size_t)num_seqs * num_heads * g.max_parts;
+  a.ws_ml = g.ws_bytes ? reinterpret_cast<float *>(const_cast<void *>(workspace)) : nullptr;
+  a.ws_acc = g.ws_bytes ? reinterpret_cast<float *>(reinterpret_cast<char *>(const_cast<void *>(workspace)) +
+                                                    rows * 2 * sizeof(float))
+                        : nullptr;
+  return a;
+}
+
+pa_status check_workspace(const DecodeGeometry &g, const void *workspace, size_t workspace_bytes) {
+  if (g.ws_bytes == 0) return PA_OK;
+  if (!workspace)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes required (%d partitions of %d tokens)", g.ws_bytes,
+                g.max_parts, g.part_tokens);
+  if (workspace_bytes < g.ws_bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, g.ws_bytes);
+  if (!aligned16(workspace)) return fail(PA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char *pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+const char *pa_last_error(void) { return g_last_error.c_str(); }
+
+pa_status pa_reshape_and_cache(const void *key, const void *value, int64_t key_token_stride,
+                               int64_t value_token_stride, void *k_cache, void *v_cache,
+                               const int64_t *slot_mapping, int64_t num_tokens, int32_t num_heads,
+                               int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                               void *stream) {
+  if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "dtype %d is not one of PA_F32/PA_F16/PA_BF16", dtype);
+  if (num_tokens < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "sizes must be positive (num_tokens >= 0)");
+  const int64_t eb = elt_bytes(dtype);
+  const int64_t row_bytes = head_dim * eb;
+  if (row_bytes % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim * element size (%lld bytes) must be a multiple of 16",
+                (long long)row_bytes);
+  if (row_bytes > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "head_dim too large");
+  if (key_token_stride < (int64_t)num_heads * head_dim || value_token_stride < (int64_t)num_heads * head_dim)
+    return fail(PA_ERR_INVALID_ARG, "token strides (%lld, %lld) smaller than num_heads*head_dim %lld",
+                (long long)key_token_stride, (long long)value_token_stride, (long long)num_heads * head_dim);
+  if ((key_token_stride * eb) % 16 != 0 || (value_token_stride * eb) % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG, "token strides must be multiples of 16 bytes");
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_INVALID_ARG, "key, value and caches must be 16-byte aligned");
+  return hip_status(pa::launch_reshape_and_cache(key, value, key_token_stride * eb, value_token_stride * eb,
+                                                 k_cache, v_cache, slot_mapping, num_tokens, num_heads,
+                                                 (int32_t)row_bytes, block_size, num_blocks,
+                                                 reinterpret_cast<hipStream_t>(stream)),
+                    "reshape_and_cache");
+}
+
+int32_t pa_decode_partition_size(int32_t max_context_len, int32_t block_size) {
+  (void)max_context_len;
+  if (block_size <= 0) return 0;
+  return default_partition(block_size);
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
+                                 int32_t block_size, int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_context_len <= 0) return 0;
+  return geometry(num_seqs, num_heads, head_dim, max_context_len, -1, block_size, partition_size).ws_bytes;
+}
+
+static pa_status decode_impl(bool run_parts, bool run_reduce, void *out, const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                             int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                             float scale, pa_dtype dtype, int32_t partition_size, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  pa_status st = check_decode_common(k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                                     max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks,
+                                     dtype, partition_size);
+  if (st != PA_OK) return st;
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  if (num_seqs > 0 && (!out || !q)) return fail(PA_ERR_INVALID_ARG, "null out or q pointer");
+  if (!aligned16(out) || !aligned16(q)) return fail(PA_ERR_INVALID_ARG, "out and q must be 16-byte aligned");
+  const DecodeGeometry g =
+      geometry(num_seqs, num_heads, head_dim, max_context_len, max_blocks_per_seq, block_size, partition_size);
+  if (g.max_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "more than 65535 partitions");
+  st = check_workspace(g, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return ok();
+  const pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                                       num_seqs, num_heads, num_blocks, scale, g, workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (run_parts) {
+    st = hip_status(pa::launch_decode_partitions(a, dtype, head_dim, block_size, s), "decode partitions");
+    if (st != PA_OK) return st;
+  }
+  if (run_reduce) {
+    st = hip_status(pa::launch_decode_reduce(a, dtype, head_dim, s), "decode reduce");
+    if (st != PA_OK) return st;
+  }
+  return ok();
+}
+
+pa_status pa_paged_attention_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                                    int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                    float scale, pa_dtype dtype, int32_t partition_size, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+  return decode_impl(true, true, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks, scale, dtype,
+                     partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_paged_attention_decode_partitions(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                               const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                               const int32_t *context_lens, int32_t max_context_len,
+                                               int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                               int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
+                                               int32_t partition_size, void *workspace, size_t workspace_bytes,
+                                               void *stream) {
+  return decode_impl(true, false, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks, scale, dtype,
+                     partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_paged_attention_decode_reduce(void *out, const int32_t *context_lens, int32_t max_context_len,
+                                           int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_heads,
+                                           int32_t head_dim, int32_t block_size, pa_dtype dtype,
+                                           int32_t partition_size, const void *workspace, size_t workspace_bytes,
+                                           void *stream) {
+  if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "dtype %d is not one of PA_F32/PA_F16/PA_BF16", dtype);
+  if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 ||
+      max_context_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "sizes must be positive (num_seqs >= 0, max_context_len >= 0)");
+  if (!pa::decode_supported(dtype, head_dim, block_size))
+    return fail(PA_ERR_UNSUPPORTED, "decode is built for head_dim 64/128 and block_size 4/8/16/32");
+  if (num_seqs > 65535 || num_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "grid dimension exceeds 65535");
+  if (partition_size != 0) {
+    pa_status st = check_partition(partition_size, block_size);
+    if (st != PA_OK) return st;
+  }
+  const DecodeGeometry g =
+      geometry(num_seqs, num_heads, head_dim, max_context_len, max_blocks_per_seq, block_size, partition_size);
+  pa_status st = check_workspace(g, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0 || g.max_parts <= 1) return ok();
+  if (!out || !context_lens) return fail(PA_ERR_INVALID_ARG, "null out or context-length pointer");
+  if (!aligned16(out)) return fail(PA_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  const pa::DecodeArgs a = decode_args(out, nullptr, nullptr, nullptr, nullptr, max_blocks_per_seq, context_lens,
+                                       num_seqs, num_heads, 1, 1.f, g, workspace);
+  return hip_status(pa::launch_decode_reduce(a, dtype, head_dim, reinterpret_cast<hipStream_t>(stream)),
+                    "decode reduce");
+}
+
+pa_status pa_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t num_layers,
+                         const int64_t *block_mapping, int64_t num_pairs, int64_t block_bytes, int64_t num_blocks,
+                         void *stream) {
+  if (num_layers <= 0 || num_pairs < 0 || block_bytes <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_layers, block_bytes and num_blocks must be positive, num_pairs >= 0");
+  if (block_bytes % 16 != 0) return fail(PA_ERR_INVALID_ARG, "block_bytes %lld is not a multiple of 16",
+                                         (long long)block_bytes);
+  if (num_pairs == 0) return ok();
+  if (!k_caches || !v_caches || !block_mapping) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  for (int32_t l = 0; l < num_layers; ++l) {
+    if (!k_caches[l] || !v_caches[l]) return fail(PA_ERR_INVALID_ARG, "layer %d: null cache pointer", l);
+    if (!aligned16(k_caches[l]) || !aligned16(v_caches[l]))
+      return fail(PA_ERR_INVALID_ARG, "layer %d: caches must be 16-byte aligned", l);
+  }
+  return hip_status(pa::launch_copy_blocks(k_caches, v_caches, num_layers, block_mapping, num_pairs, block_bytes,
+                                           num_blocks, reinterpret_cast<hipStream_t>(stream)),
+                    "copy_blocks");
+}
+
+pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32_t *cu_q_lens, const void *k_cache,
+                                           const void *v_cache, const int32_t *block_tables,
+                                           int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                           int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                           int32_t max_context_len, int32_t num_heads, int32_t head_dim,
+                                           int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
+                                           void *stream) {
+  if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "dtype %d is not one of PA_F32/PA_F16/PA_BF16", dtype);
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_context_len < 0 || num_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARG, "sizes must be positive (num_seqs, total_q, max_q_len, max_context_len >= 0)");
+  if (!pa::prefill_supported(dtype, head_dim, block_size))
+    return fail(PA_ERR_UNSUPPORTED, "prefill chunk is built for fp16/bf16, head_dim 128, block_size 16/32 "
+                "(got dtype %d, head_dim %d, block_size %d)", dtype, head_dim, block_size);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  if (num_seqs > 65535 || num_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "grid dimension exceeds 65535");
+  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return ok();
+  if (!out || !q || !cu_q_lens || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_INVALID_ARG, "out, q and caches must be 16-byte aligned");
+  pa::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.cu_q_lens = cu_q_lens;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_heads = num_heads;
+  int64_t cap = max_context_len;
+  if ((int64_t)max_blocks_per_seq * block_size < cap) cap = (int64_t)max_blocks_per_seq * block_size;
+  a.ctx_cap = (int32_t)cap;
+  a.scale_log2 = scale * kLog2e;
+  return hip_status(pa::launch_prefill_chunk(a, dtype, head_dim, block_size, reinterpret_cast<hipStream_t>(stream)),
+                    "prefill chunk");
+}
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+// Cache write through a slot mapping, and batched whole-block copy.
+//
+// Both are pure byte moves (no arithmetic, no conversion), so they are
+// bit-exact for every dtype.  Both are the fused single-launch kernels the
+// Korean review of the vLLM paper (mz-moonzoo.tistory.com/116, section 5.1,
+// items 1 and 3) describes: the write replaces a split/reshape/scatter
+// sequence, and the copy replaces one small memcpy per block.
+//
+// gfx950 mapping: every lane moves 16 bytes per instruction
+// (global_load_dwordx4 / global_store_dwordx4); consecutive lanes touch
+// consecutive 16-byte chunks of a row or block, so every wave access is a
+// contiguous 1 KB run (or a whole 256 B token row per 16 lanes).
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+constexpr int kCacheThreads = 256;
+
+// One workgroup per new token: copy its num_heads K rows and V rows into
+// (slot / B, h, slot % B).  Rows are row_bytes long, a multiple of 16.
+__global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(
+    const char *__restrict__ key, const char *__restrict__ value, int64_t key_stride_bytes,
+    int64_t value_stride_bytes, char *__restrict__ k_cache, char *__restrict__ v_cache,
+    const int64_t *__restrict__ slot_mapping, int32_t num_heads, int32_t row_bytes, int32_t block_size,
+    int64_t num_slots) {
+  const int64_t t = blockIdx.x;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / block_size;
+  const int64_t off = slot % block_size;
+  const int chunks_per_row = row_bytes >> 4;
+  const int per_tensor = num_heads * chunks_per_row;
+  for (int idx = threadIdx.x; idx < 2 * per_tensor; idx += kCacheThreads) {
+    const bool is_v = idx >= per_tensor;
+    const int r = is_v ? idx - per_tensor : idx;
+    const int h = r / chunks_per_row;
+    const int c = r - h * chunks_per_row;
+    const char *src = (is_v ? value + t * value_stride_bytes : key + t * key_stride_bytes) +
+                      (int64_t)h * row_bytes + c * 16;
+    char *dst = (is_v ? v_cache : k_cache) + ((blk * num_heads + h) * block_size + off) * row_bytes + c * 16;
+    *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+  }
+}
+
+hipError_t launch_reshape_and_cache(const void *key, const void *value, int64_t key_stride_bytes,
+                                    int64_t value_stride_bytes, void *k_cache, void *v_cache,
+                                    const int64_t *slot_mapping, int64_t num_tokens, int32_t num_heads,
+                                    int32_t row_bytes, int32_t block_size, int64_t num_blocks,
+                                    hipStream_t stream) {
+  // grid.x is at most 2^31-1; split very long mappings into several launches.
+  const int64_t kMaxGrid = 0x7fffffff;
+  for (int64_t first = 0; first < num_tokens; first += kMaxGrid) {
+    const int64_t count = num_tokens - first < kMaxGrid ? num_tokens - first : kMaxGrid;
+    hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)count), dim3(kCacheThreads), 0, stream,
+                       reinterpret_cast<const char *>(key) + first * key_stride_bytes,
+                       reinterpret_cast<const char *>(value) + first * value_stride_bytes, key_stride_bytes,
+                       value_stride_bytes, reinterpret_cast<char *>(k_cache), reinterpret_cast<char *>(v_cache),
+                       slot_mapping + first, num_heads, row_bytes, block_size, num_blocks * block_size);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------- copy_blocks
+
+struct LayerPtrs {
+  char *k[kCopyMaxLayers];
+  char *v[kCopyMaxLayers];
+};
+
+constexpr int kCopyUnroll = 4;
+constexpr int64_t kCopyChunk = (int64_t)kCacheThreads * 16 * kCopyUnroll;  // bytes per workgroup
+
+// grid.x = pair * chunks_per_block + chunk, grid.y = 2 * layer + (K=0 / V=1).
+__global__ __launch_bounds__(kCacheThreads) void copy_blocks_kernel(LayerPtrs ptrs,
+                                                                    const int64_t *__restrict__ mapping,
+                                                                    int64_t block_bytes, int64_t num_blocks,
+                                                                    int32_t chunks_per_block) {
+  const int64_t pair = blockIdx.x / chunks_per_block;
+  const int64_t chunk = blockIdx.x - pair * chunks_per_block;
+  const int layer = blockIdx.y >> 1;
+  char *base = (blockIdx.y & 1) ? ptrs.v[layer] : ptrs.k[layer];
+  const int64_t src = mapping[2 * pair];
+  const int64_t dst = mapping[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const char *from = base + src * block_bytes;
+  char *to = base + dst * block_bytes;
+  const int64_t begin = chunk * kCopyChunk;
+  uint4 r[kCopyUnroll];
+  bool live[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t o = begin + ((int64_t)u * kCacheThreads + threadIdx.x) * 16;
+    live[u] = o < block_bytes;
+    if (live[u]) r[u] = *reinterpret_cast<const uint4 *>(from + o);
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t o = begin + ((int64_t)u * kCacheThreads + threadIdx.x) * 16;
+    if (live[u]) *reinterpret_cast<uint4 *>(to + o) = r[u];
+  }
+}
+
+hipError_t launch_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t num_layers,
+                              const int64_t *block_mapping, int64_t num_pairs, int64_t block_bytes,
+                              int64_t num_blocks, hipStream_t stream) {
+  const int64_t chunks = (block_bytes + kCopyChunk - 1) / kCopyChunk;
+  const int64_t max_pairs = 0x7fffffff / chunks;
+  for (int32_t l0 = 0; l0 < num_layers; l0 += kCopyMaxLayers) {
+    const int32_t nl = num_layers - l0 < kCopyMaxLayers ? num_layers - l0 : kCopyMaxLayers;
+    LayerPtrs p = {};
+    for (int32_t i = 0; i < nl; ++i) {
+      p.k[i] = reinterpret_cast<char *>(k_caches[l0 + i]);
+      p.v[i] = reinterpret_cast<char *>(v_caches[l0 + i]);
+    }
+    for (int64_t first = 0; first < num_pairs; first += max_pairs) {
+      const int64_t np = num_pairs - first < max_pairs ? num_pairs - first : max_pairs;
+      dim3 grid((unsigned)(np * chunks), (unsigned)(2 * nl));
+      hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kCacheThreads), 0, stream, p, block_mapping + 2 * first,
+                         block_bytes, num_blocks, (int32_t)chunks);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace pa

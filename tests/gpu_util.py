@@ -1,0 +1,77 @@
+"""Helpers for the GPU parity tests: moving workload arrays to the device and
+the attention tolerance.
+
+Tolerance for attention outputs (fp16/bf16 in, fp32 accumulate): an element
+passes if |gpu - ref| <= 2e-3 or |gpu - ref| <= 1e-2 * |ref|, where ref is the
+float64 oracle value rounded to the output dtype. fp32 outputs use
+|gpu - ref| <= 1e-5 or <= 1e-4 * |ref| (float32 accumulation over at most a few
+thousand terms of magnitude O(1)).
+"""
+import sys
+
+import numpy as np
+import torch
+
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+TOL = {"f32": (1e-5, 1e-4), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2)}
+
+
+def say(*args):
+    print(*args, flush=True)
+    sys.stdout.flush()
+
+
+def dev(arr: np.ndarray, dtype: str = None) -> torch.Tensor:
+    """numpy storage array -> device tensor (bf16 from its uint16 bits)."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def host(t: torch.Tensor, dtype: str) -> np.ndarray:
+    """device tensor -> numpy storage array (bf16 as uint16 bits)."""
+    t = t.detach().cpu().contiguous()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def as_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().double().numpy()
+
+
+def rounded(ref: np.ndarray, dtype: str) -> np.ndarray:
+    return torch.from_numpy(ref).to(TORCH_DT[dtype]).double().numpy()
+
+
+def check_attention(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str = ""):
+    """Assert the tolerance above elementwise; return (max_abs, max_rel)."""
+    atol, rtol = TOL[dtype]
+    g = as_f64(got)
+    r = rounded(ref, dtype)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    err = np.abs(g - r)
+    ok = (err <= atol) | (err <= rtol * np.abs(r))
+    big = np.abs(r) >= atol
+    max_abs = float(err.max()) if err.size else 0.0
+    max_rel = float((err[big] / np.abs(r[big])).max()) if big.any() else 0.0
+    if not ok.all():
+        idx = np.unravel_index(np.argmax(np.where(ok, 0, err)), err.shape)
+        raise AssertionError(f"{what}: {int((~ok).sum())} of {ok.size} elements out of tolerance; "
+                             f"worst at {idx}: gpu {g[idx]!r} ref {r[idx]!r}; max_abs {max_abs:.3g} "
+                             f"max_rel {max_rel:.3g}; nan in gpu: {bool(np.isnan(g).any())}")
+    return max_abs, max_rel
+
+
+class DeviceCase:
+    """A workloads.PagedCase with its tensors on the GPU."""
+
+    def __init__(self, case):
+        self.case = case
+        dt = case.dtype
+        self.q = dev(case.q, dt)
+        self.k_cache = dev(case.k_cache, dt)
+        self.v_cache = dev(case.v_cache, dt)
+        self.block_tables = dev(case.block_tables)
+        self.context_lens = dev(case.context_lens)
+        self.out = torch.empty_like(self.q)
