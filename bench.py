@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--workload", default="opt13b_b64", choices=["opt13b_b64", "large_batch_b256"])
     ap.add_argument("--replicas", type=int, default=2,
                     help="copies of the KV pool used in turn, so no step finds the last one's data in cache")
-    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--split-workers", type=int, default=0,
+                    help="worker waves the tile stream is cut among (0: as many as the GPU holds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-runs", type=int, default=3)
     return ap.parse_args()
@@ -100,8 +101,8 @@ def main():
     new_k, new_v = to_dev(case.new_key, case.dtype), to_dev(case.new_value, case.dtype)
     out = torch.empty_like(q)
     max_ctx = case.max_context_len
-    part = args.partition_size
-    ws = pa.alloc_decode_workspace(S, H, D, max_ctx, B, part, device=dev)
+    workers = args.split_workers
+    ws = pa.alloc_decode_workspace(S, H, D, max_ctx, B, workers, device=dev)
     stream = torch.cuda.current_stream()
 
     # Calibration kernel for the HBM byte counters: a plain 1 GiB copy.
@@ -124,11 +125,11 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         pa.paged_attention_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, max_ctx,
-                                             case.scale, workspace=ws, partition_size=part)
+                                             case.scale, workspace=ws, split_workers=workers)
         if ev is not None:
             ev[1].record(stream)
         pa.paged_attention_decode_reduce(out, context_lens, max_ctx, case.max_blocks_per_seq, H, D, B,
-                                         workspace=ws, partition_size=part)
+                                         workspace=ws, split_workers=workers)
 
     for i in range(args.warmup):
         step(i)
@@ -144,7 +145,7 @@ def main():
     ms_per_step = start.elapsed_time(end) / args.steps
     part_ms = [a.elapsed_time(b) for a, b in evs]
     part_avg_s = float(np.mean(part_ms)) * 1e-3
-    print(f"[bench] step {ms_per_step * 1e3:.1f} us; partition kernel avg {part_avg_s * 1e6:.1f} us "
+    print(f"[bench] step {ms_per_step * 1e3:.1f} us; partition pass avg {part_avg_s * 1e6:.1f} us "
           f"(min {min(part_ms) * 1e3:.1f}, max {max(part_ms) * 1e3:.1f})", file=sys.stderr, flush=True)
 
     elt = case.elt_bytes
@@ -190,7 +191,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": case.name, "num_seqs": S, "num_heads": H, "head_dim": D, "block_size": B,
                    "context_tokens": int(case.context_lens.sum()), "max_context_len": max_ctx,
-                   "partition_size": part or pa.decode_partition_size(max_ctx, B), "pool_replicas": args.replicas,
+                   "split_workers": workers or pa.decode_default_workers(tdt, D, B), "pool_replicas": args.replicas,
                    "step": "reshape_and_cache(new tokens) + decode partitions + decode reduce"},
         "effective_kv_gbps": kv_bytes / (ms_per_step * 1e-3) / 1e9,
         "pct_hbm_peak": kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,

@@ -104,27 +104,33 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, int64_t key_t
                                pa_dtype dtype, void *stream);
 
 /*
- * Decode attention is split into a partition pass and a reduce pass.  The
- * context of a sequence is cut into partitions of partition_size tokens;
- * each partition is attended independently (the block-separability of the
- * attention sum, review section 4.1) and the partial results -- running max
- * m, running sum l and the unnormalised weighted value sum -- are merged by
- * the reduce pass.  When max_context_len <= partition_size no workspace is
- * needed and the partition pass writes the output itself.
+ * Decode attention runs as a partition pass and a reduce pass.  Attention
+ * over a context splits by block (review section 4.1): any run of
+ * consecutive positions can be attended on its own, giving a running max m,
+ * a running sum l and an unnormalised weighted value sum, and such pieces
+ * merge exactly by rescaling to a common max.  The partition pass cuts the
+ * whole batch -- every (sequence, head, 16-token tile) -- into equal
+ * contiguous ranges, one per worker wave, so that every wave reads the same
+ * number of K/V bytes whatever the mix of context lengths.  A (sequence,
+ * head) pair that lies inside one range is finished by its wave; a pair cut
+ * by range boundaries leaves partial results that the reduce pass merges.
  *
- * partition_size: 0 lets the library choose (pa_decode_partition_size);
- * otherwise a positive multiple of 16 and of block_size.
+ * split_workers: 0 lets the library use as many worker waves as the device
+ * holds at once (pa_decode_default_workers); a positive value uses at most
+ * that many.  The result does not depend on it beyond floating-point
+ * rounding; tests use it to move the cut points.
  */
-int32_t pa_decode_partition_size(int32_t max_context_len, int32_t block_size);
+int32_t pa_decode_default_workers(pa_dtype dtype, int32_t head_dim, int32_t block_size);
 
-/* Workspace bytes pa_paged_attention_decode needs (0 when one partition
- * covers max_context_len).  Layout: fp32 (m, l) pairs
- * [num_seqs][num_heads][P_max] followed by fp32 partial sums
- * [num_seqs][num_heads][P_max][head_dim], P_max = ceil(max_context_len /
- * partition_size).  Its contents need no initialisation. */
+/* Workspace bytes pa_paged_attention_decode needs for up to split_workers
+ * worker waves (0: an upper bound for the current device); 0 only for
+ * num_seqs 0.  Layout: the work plan (uint32: 4 header words plus two per
+ * worker, padded to 256 bytes), then two fp32 partial results of head_dim + 2
+ * floats per worker.  Its contents need no initialisation; calls that share
+ * one workspace must be ordered on one stream. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t block_size,
-                                 int32_t partition_size);
+                                 int32_t split_workers);
 
 /*
  * pa_paged_attention_decode -- one query per sequence over its paged KV.
@@ -143,33 +149,35 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t he
  *  max_context_len  host upper bound of context_lens (sizes the grid).
  *  scale            softmax scale, normally 1/sqrt(head_dim).
  *  workspace        device, >= pa_decode_workspace_bytes(...) bytes, 16-byte
- *                   aligned; may be NULL when that size is 0.
+ *                   aligned; may be NULL only when num_seqs is 0.
  */
 pa_status pa_paged_attention_decode(void *out, const void *q, const void *k_cache,
                                     const void *v_cache, const int32_t *block_tables,
                                     int32_t max_blocks_per_seq, const int32_t *context_lens,
                                     int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
                                     int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                                    float scale, pa_dtype dtype, int32_t partition_size,
+                                    float scale, pa_dtype dtype, int32_t split_workers,
                                     void *workspace, size_t workspace_bytes, void *stream);
 
-/* The partition pass alone (same arguments).  Writes `out` for sequences with
- * at most one partition and the workspace for the others. */
+/* The partition pass alone (same arguments).  Writes `out` for every pair
+ * that one worker wave finished and the workspace (plan and partial
+ * results) for the others. */
 pa_status pa_paged_attention_decode_partitions(
     void *out, const void *q, const void *k_cache, const void *v_cache, const int32_t *block_tables,
     int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
     int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-    float scale, pa_dtype dtype, int32_t partition_size, void *workspace, size_t workspace_bytes,
+    float scale, pa_dtype dtype, int32_t split_workers, void *workspace, size_t workspace_bytes,
     void *stream);
 
-/* The reduce pass alone: merges the partials of sequences with two or more
- * partitions into `out`.  A no-op when max_context_len <= partition_size.
- * Arguments as for pa_paged_attention_decode (same partition_size). */
+/* The reduce pass alone: merges the partial results of the pairs the
+ * partition pass left cut into `out`.  Arguments as for
+ * pa_paged_attention_decode; it must see the same split_workers and the
+ * workspace the partition pass wrote. */
 pa_status pa_paged_attention_decode_reduce(void *out, const int32_t *context_lens,
                                            int32_t max_context_len, int32_t max_blocks_per_seq,
                                            int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                            int32_t block_size, pa_dtype dtype,
-                                           int32_t partition_size, const void *workspace,
+                                           int32_t split_workers, const void *workspace,
                                            size_t workspace_bytes, void *stream);
 
 /*

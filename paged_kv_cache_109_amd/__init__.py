@@ -12,7 +12,7 @@ from ._binding import (  # noqa: F401
     abi_version,
     alloc_decode_workspace,
     copy_blocks,
-    decode_partition_size,
+    decode_default_workers,
     decode_workspace_bytes,
     paged_attention_decode,
     paged_attention_decode_partitions,

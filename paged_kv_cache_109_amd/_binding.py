@@ -31,7 +31,7 @@ _SIGS = {
     "pa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "pa_last_error": ([], ctypes.c_char_p),
     "pa_reshape_and_cache": ([P, P, i64, i64, P, P, P, i64, i32, i32, i32, i64, ctypes.c_int, P], ctypes.c_int),
-    "pa_decode_partition_size": ([i32, i32], i32),
+    "pa_decode_default_workers": ([ctypes.c_int, i32, i32], i32),
     "pa_decode_workspace_bytes": ([i32, i32, i32, i32, i32, i32], sz),
     "pa_paged_attention_decode": (
         [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, i32, P, sz, P], ctypes.c_int),
@@ -121,24 +121,25 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Ten
         _pa_dtype(k_cache), _stream(stream)), "reshape_and_cache")
 
 
-def decode_partition_size(max_context_len: int, block_size: int) -> int:
-    return int(_lib.pa_decode_partition_size(int(max_context_len), int(block_size)))
+def decode_default_workers(dtype: torch.dtype, head_dim: int, block_size: int) -> int:
+    """Worker waves a decode call uses when split_workers is 0 (current device)."""
+    return int(_lib.pa_decode_default_workers(_DTYPE[dtype], int(head_dim), int(block_size)))
 
 
 def decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
-                           block_size: int, partition_size: int = 0) -> int:
+                           block_size: int, split_workers: int = 0) -> int:
     return int(_lib.pa_decode_workspace_bytes(int(num_seqs), int(num_heads), int(head_dim),
-                                              int(max_context_len), int(block_size), int(partition_size)))
+                                              int(max_context_len), int(block_size), int(split_workers)))
 
 
-def alloc_decode_workspace(num_seqs, num_heads, head_dim, max_context_len, block_size, partition_size=0,
+def alloc_decode_workspace(num_seqs, num_heads, head_dim, max_context_len, block_size, split_workers=0,
                            device="cuda") -> Optional[torch.Tensor]:
-    n = decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, block_size, partition_size)
+    n = decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, block_size, split_workers)
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
 def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-                 partition_size, workspace, stream):
+                 split_workers, workspace, stream):
     N, H, B, D = _cache_dims(k_cache, v_cache)
     S = int(q.shape[0])
     if q.shape != (S, H, D) or out.shape != (S, H, D) or q.dtype != k_cache.dtype or out.dtype != q.dtype:
@@ -151,41 +152,41 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_conte
     return (_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
             _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
             _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, H, D, B, N, float(scale),
-            _pa_dtype(q), int(partition_size), ws_ptr, ws_bytes, _stream(stream))
+            _pa_dtype(q), int(split_workers), ws_ptr, ws_bytes, _stream(stream))
 
 
 def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
-                           scale: float, workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
+                           scale: float, workspace: Optional[torch.Tensor] = None, split_workers: int = 0,
                            stream=None) -> torch.Tensor:
     """out[s, h] = softmax(scale * q[s, h] . K) V over the first context_lens[s]
-    positions of sequence s, read through block_tables. Allocates the split-KV
+    positions of sequence s, read through block_tables. Allocates the
     workspace with torch when none is given."""
     if workspace is None:
         workspace = alloc_decode_workspace(q.shape[0], k_cache.shape[1], k_cache.shape[3], max_context_len,
-                                           k_cache.shape[2], partition_size, device=q.device)
+                                           k_cache.shape[2], split_workers, device=q.device)
     _check(_lib.pa_paged_attention_decode(*_decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
-                                                        max_context_len, scale, partition_size, workspace,
+                                                        max_context_len, scale, split_workers, workspace,
                                                         stream)), "paged_attention_decode")
     return out
 
 
 def paged_attention_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
-                                      scale, workspace=None, partition_size=0, stream=None) -> None:
+                                      scale, workspace=None, split_workers=0, stream=None) -> None:
     _check(_lib.pa_paged_attention_decode_partitions(*_decode_args(
-        out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale, partition_size, workspace,
+        out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale, split_workers, workspace,
         stream)), "paged_attention_decode_partitions")
 
 
 def paged_attention_decode_reduce(out, context_lens, max_context_len, max_blocks_per_seq, num_heads, head_dim,
-                                  block_size, workspace=None, partition_size=0, stream=None) -> None:
+                                  block_size, workspace=None, split_workers=0, stream=None) -> None:
     S = int(context_lens.shape[0])
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.pa_paged_attention_decode_reduce(
         _dev(out, "out"), _dev(context_lens, "context_lens", torch.int32), int(max_context_len),
         int(max_blocks_per_seq), S, int(num_heads), int(head_dim), int(block_size), _pa_dtype(out),
-        int(partition_size), ws_ptr, ws_bytes, _stream(stream)), "paged_attention_decode_reduce")
+        int(split_workers), ws_ptr, ws_bytes, _stream(stream)), "paged_attention_decode_reduce")
 
 
 def copy_blocks(k_caches: Sequence[torch.Tensor], v_caches: Sequence[torch.Tensor], block_mapping: torch.Tensor,

@@ -8,6 +8,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <algorithm>
 #include <cstdio>
 #include <string>
 
@@ -47,52 +48,55 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Default tokens per decode partition: 512 tokens (32 blocks of 16), kept a
-// multiple of 16 and of B and within one table entry per lane.
-int32_t default_partition(int32_t block_size) {
-  int64_t p = 512;
-  if (p > (int64_t)pa::kMaxPartitionBlocks * block_size) p = (int64_t)pa::kMaxPartitionBlocks * block_size;
-  return (int32_t)p;
+// Compute units of the current device (0 when no device is usable).
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return cus;
 }
 
-pa_status check_partition(int32_t partition_size, int32_t block_size) {
-  if (partition_size <= 0 || partition_size % pa::kDecodeTile != 0 || partition_size % block_size != 0)
-    return fail(PA_ERR_INVALID_ARG, "partition_size %d must be a positive multiple of %d and of block_size %d",
-                partition_size, pa::kDecodeTile, block_size);
-  if ((int64_t)partition_size > (int64_t)pa::kMaxPartitionBlocks * block_size)
-    return fail(PA_ERR_INVALID_ARG, "partition_size %d spans more than %d blocks of %d", partition_size,
-                pa::kMaxPartitionBlocks, block_size);
-  return PA_OK;
+// Worker waves the workspace must hold for `split_workers` (0 = device default).
+int64_t worker_bound(int32_t split_workers) {
+  if (split_workers > 0) return split_workers;
+  const int cus = device_cus();
+  return (int64_t)(cus > 0 ? cus : 1024) * pa::kMaxWavesPerCu;
 }
 
 struct DecodeGeometry {
   int32_t ctx_cap;
-  int32_t part_tokens;
-  int32_t max_parts;
-  size_t ws_bytes;
+  int64_t workers;     // worker waves used by the partition pass
+  size_t plan_bytes;   // header + per-worker starts
+  size_t ws_bytes;     // plan + two fragments per worker
 };
 
-DecodeGeometry geometry(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
-                        int32_t max_blocks, int32_t block_size, int32_t partition_size) {
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+DecodeGeometry geometry(int32_t head_dim, int32_t max_context_len, int32_t max_blocks, int32_t block_size,
+                        int64_t workers) {
   DecodeGeometry g;
   int64_t cap = max_context_len;
   if (max_blocks >= 0 && (int64_t)max_blocks * block_size < cap) cap = (int64_t)max_blocks * block_size;
   g.ctx_cap = (int32_t)(cap < 0 ? 0 : cap);
-  g.part_tokens = partition_size > 0 ? partition_size : default_partition(block_size);
-  g.max_parts = (int32_t)ceil_div(g.ctx_cap > 0 ? g.ctx_cap : 1, g.part_tokens);
-  if (g.max_parts <= 1) {
-    g.ws_bytes = 0;
-  } else {
-    const size_t rows = (size_t)num_seqs * num_heads * g.max_parts;
-    g.ws_bytes = rows * 2 * sizeof(float) + rows * (size_t)head_dim * sizeof(float);
-  }
+  g.workers = workers;
+  g.plan_bytes = round_up(((size_t)pa::kPlanHeader + 2 * (size_t)workers) * sizeof(uint32_t), 256);
+  g.ws_bytes = g.plan_bytes + (size_t)workers * 2 * ((size_t)head_dim + 2) * sizeof(float);
   return g;
+}
+
+// Worker waves a decode call launches: as many as fit on the device at
+// once, or split_workers when that is smaller.
+int64_t decode_workers(pa_dtype dtype, int32_t head_dim, int32_t block_size, int32_t split_workers) {
+  const int64_t fit = (int64_t)device_cus() * pa::decode_waves_per_cu(dtype, head_dim, block_size);
+  int64_t w = fit > 0 ? fit : 1;
+  if (split_workers > 0 && split_workers < w) w = split_workers;
+  return w;
 }
 
 pa_status check_decode_common(const void *k_cache, const void *v_cache, const int32_t *block_tables,
                               int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
                               int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size,
-                              int64_t num_blocks, pa_dtype dtype, int32_t partition_size) {
+                              int64_t num_blocks, pa_dtype dtype, int32_t split_workers) {
   if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "dtype %d is not one of PA_F32/PA_F16/PA_BF16", dtype);
   if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || max_context_len < 0)
@@ -109,20 +113,23 @@ pa_status check_decode_common(const void *k_cache, const void *v_cache, const in
   if (num_seqs > 0 && (!k_cache || !v_cache || !block_tables || !context_lens))
     return fail(PA_ERR_INVALID_ARG, "null cache, block table or context-length pointer");
   if (!aligned16(k_cache) || !aligned16(v_cache)) return fail(PA_ERR_INVALID_ARG, "caches must be 16-byte aligned");
-  if (partition_size != 0) {
-    pa_status st = check_partition(partition_size, block_size);
-    if (st != PA_OK) return st;
-  }
-  (void)elt_bytes(dtype);
+  if (split_workers < 0) return fail(PA_ERR_INVALID_ARG, "split_workers %d must be >= 0", split_workers);
+  // Tile indices of the whole batch must fit 31 bits.
+  const int64_t cap = std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * block_size);
+  if ((int64_t)num_seqs * num_heads * ((cap + pa::kDecodeTile - 1) / pa::kDecodeTile) >= ((int64_t)1 << 31))
+    return fail(PA_ERR_UNSUPPORTED, "num_seqs * num_heads * ceil(context/16) must be below 2^31");
   return PA_OK;
 }
 
 pa::DecodeArgs decode_args(void *out, const void *q, const void *k_cache, const void *v_cache,
                            const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
-                           int32_t num_seqs, int32_t num_heads, int64_t num_blocks, float scale,
-                           const DecodeGeometry &g, const void *workspace) {
+                           int32_t num_seqs, int32_t num_heads, int32_t head_dim, pa_dtype dtype,
+                           int64_t num_blocks, float scale, const DecodeGeometry &g, const void *workspace) {
   pa::DecodeArgs a;
+  char *ws = reinterpret_cast<char *>(const_cast<void *>(workspace));
   a.out = out;
+  a.plan = reinterpret_cast<uint32_t *>(ws);
+  a.frags = reinterpret_cast<float *>(ws + g.plan_bytes);
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
@@ -133,22 +140,16 @@ pa::DecodeArgs decode_args(void *out, const void *q, const void *k_cache, const 
   a.max_blocks = max_blocks_per_seq;
   a.num_heads = num_heads;
   a.ctx_cap = g.ctx_cap;
-  a.part_tokens = g.part_tokens;
-  a.max_parts = g.max_parts;
+  a.workers = (int32_t)g.workers;
+  a.out_row_words = (int32_t)((int64_t)num_heads * head_dim * elt_bytes(dtype) / 4);
   a.scale_log2 = scale * kLog2e;
-  const size_t rows = (size_t)num_seqs * num_heads * g.max_parts;
-  a.ws_ml = g.ws_bytes ? reinterpret_cast<float *>(const_cast<void *>(workspace)) : nullptr;
-  a.ws_acc = g.ws_bytes ? reinterpret_cast<float *>(reinterpret_cast<char *>(const_cast<void *>(workspace)) +
-                                                    rows * 2 * sizeof(float))
-                        : nullptr;
   return a;
 }
 
 pa_status check_workspace(const DecodeGeometry &g, const void *workspace, size_t workspace_bytes) {
-  if (g.ws_bytes == 0) return PA_OK;
   if (!workspace)
-    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes required (%d partitions of %d tokens)", g.ws_bytes,
-                g.max_parts, g.part_tokens);
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes required (%lld worker waves)", g.ws_bytes,
+                (long long)g.workers);
   if (workspace_bytes < g.ws_bytes)
     return fail(PA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, g.ws_bytes);
   if (!aligned16(workspace)) return fail(PA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
@@ -205,39 +206,39 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, int64_t key_t
                     "reshape_and_cache");
 }
 
-int32_t pa_decode_partition_size(int32_t max_context_len, int32_t block_size) {
-  (void)max_context_len;
-  if (block_size <= 0) return 0;
-  return default_partition(block_size);
+int32_t pa_decode_default_workers(pa_dtype dtype, int32_t head_dim, int32_t block_size) {
+  if (!valid_dtype(dtype) || !pa::decode_supported(dtype, head_dim, block_size)) return 0;
+  return (int32_t)decode_workers(dtype, head_dim, block_size, 0);
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
-                                 int32_t block_size, int32_t partition_size) {
-  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_context_len <= 0) return 0;
-  return geometry(num_seqs, num_heads, head_dim, max_context_len, -1, block_size, partition_size).ws_bytes;
+                                 int32_t block_size, int32_t split_workers) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_context_len < 0 ||
+      split_workers < 0)
+    return 0;
+  return geometry(head_dim, max_context_len, -1, block_size, worker_bound(split_workers)).ws_bytes;
 }
 
 static pa_status decode_impl(bool run_parts, bool run_reduce, void *out, const void *q, const void *k_cache,
                              const void *v_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
                              const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
                              int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                             float scale, pa_dtype dtype, int32_t partition_size, void *workspace,
+                             float scale, pa_dtype dtype, int32_t split_workers, void *workspace,
                              size_t workspace_bytes, void *stream) {
   pa_status st = check_decode_common(k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                                      max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks,
-                                     dtype, partition_size);
+                                     dtype, split_workers);
   if (st != PA_OK) return st;
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
   if (num_seqs > 0 && (!out || !q)) return fail(PA_ERR_INVALID_ARG, "null out or q pointer");
   if (!aligned16(out) || !aligned16(q)) return fail(PA_ERR_INVALID_ARG, "out and q must be 16-byte aligned");
-  const DecodeGeometry g =
-      geometry(num_seqs, num_heads, head_dim, max_context_len, max_blocks_per_seq, block_size, partition_size);
-  if (g.max_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "more than 65535 partitions");
+  if (num_seqs == 0) return ok();
+  const DecodeGeometry g = geometry(head_dim, max_context_len, max_blocks_per_seq, block_size,
+                                    decode_workers(dtype, head_dim, block_size, split_workers));
   st = check_workspace(g, workspace, workspace_bytes);
   if (st != PA_OK) return st;
-  if (num_seqs == 0) return ok();
   const pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
-                                       num_seqs, num_heads, num_blocks, scale, g, workspace);
+                                       num_seqs, num_heads, head_dim, dtype, num_blocks, scale, g, workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (run_parts) {
     st = hip_status(pa::launch_decode_partitions(a, dtype, head_dim, block_size, s), "decode partitions");
@@ -254,11 +255,11 @@ pa_status pa_paged_attention_decode(void *out, const void *q, const void *k_cach
                                     const int32_t *block_tables, int32_t max_blocks_per_seq,
                                     const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
                                     int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                                    float scale, pa_dtype dtype, int32_t partition_size, void *workspace,
+                                    float scale, pa_dtype dtype, int32_t split_workers, void *workspace,
                                     size_t workspace_bytes, void *stream) {
   return decode_impl(true, true, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                      max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks, scale, dtype,
-                     partition_size, workspace, workspace_bytes, stream);
+                     split_workers, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_paged_attention_decode_partitions(void *out, const void *q, const void *k_cache, const void *v_cache,
@@ -266,38 +267,34 @@ pa_status pa_paged_attention_decode_partitions(void *out, const void *q, const v
                                                const int32_t *context_lens, int32_t max_context_len,
                                                int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                                int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
-                                               int32_t partition_size, void *workspace, size_t workspace_bytes,
+                                               int32_t split_workers, void *workspace, size_t workspace_bytes,
                                                void *stream) {
   return decode_impl(true, false, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                      max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks, scale, dtype,
-                     partition_size, workspace, workspace_bytes, stream);
+                     split_workers, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_paged_attention_decode_reduce(void *out, const int32_t *context_lens, int32_t max_context_len,
                                            int32_t max_blocks_per_seq, int32_t num_seqs, int32_t num_heads,
                                            int32_t head_dim, int32_t block_size, pa_dtype dtype,
-                                           int32_t partition_size, const void *workspace, size_t workspace_bytes,
+                                           int32_t split_workers, const void *workspace, size_t workspace_bytes,
                                            void *stream) {
   if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "dtype %d is not one of PA_F32/PA_F16/PA_BF16", dtype);
   if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 ||
-      max_context_len < 0)
-    return fail(PA_ERR_INVALID_ARG, "sizes must be positive (num_seqs >= 0, max_context_len >= 0)");
+      max_context_len < 0 || split_workers < 0)
+    return fail(PA_ERR_INVALID_ARG, "sizes must be positive (num_seqs, max_context_len, split_workers >= 0)");
   if (!pa::decode_supported(dtype, head_dim, block_size))
     return fail(PA_ERR_UNSUPPORTED, "decode is built for head_dim 64/128 and block_size 4/8/16/32");
-  if (num_seqs > 65535 || num_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "grid dimension exceeds 65535");
-  if (partition_size != 0) {
-    pa_status st = check_partition(partition_size, block_size);
-    if (st != PA_OK) return st;
-  }
-  const DecodeGeometry g =
-      geometry(num_seqs, num_heads, head_dim, max_context_len, max_blocks_per_seq, block_size, partition_size);
+  if (num_seqs > 65535 || num_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs or num_heads exceeds 65535");
+  if (num_seqs == 0) return ok();
+  const DecodeGeometry g = geometry(head_dim, max_context_len, max_blocks_per_seq, block_size,
+                                    decode_workers(dtype, head_dim, block_size, split_workers));
   pa_status st = check_workspace(g, workspace, workspace_bytes);
   if (st != PA_OK) return st;
-  if (num_seqs == 0 || g.max_parts <= 1) return ok();
   if (!out || !context_lens) return fail(PA_ERR_INVALID_ARG, "null out or context-length pointer");
   if (!aligned16(out)) return fail(PA_ERR_INVALID_ARG, "out must be 16-byte aligned");
   const pa::DecodeArgs a = decode_args(out, nullptr, nullptr, nullptr, nullptr, max_blocks_per_seq, context_lens,
-                                       num_seqs, num_heads, 1, 1.f, g, workspace);
+                                       num_seqs, num_heads, head_dim, dtype, 1, 1.f, g, workspace);
   return hip_status(pa::launch_decode_reduce(a, dtype, head_dim, reinterpret_cast<hipStream_t>(stream)),
                     "decode reduce");
 }

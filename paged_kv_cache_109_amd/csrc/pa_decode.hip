@@ -1,5 +1,4 @@
-// Paged decode attention for gfx950: a split-KV partition pass and a reduce
-// pass.
+// Paged decode attention for gfx950: plan, stream-K partition pass, fix-up.
 //
 // What is computed (paper notes "PagedAttention: Efficient Memory Management
 // for Large Language Model Serving with PagedAttention", unpurerationalist
@@ -8,46 +7,81 @@
 // scale*q.k, then the weight-sum of the values.  The Korean review
 // (mz-moonzoo.tistory.com/116, section 4.1) points out that the sum splits
 // by block: each block's contribution can be formed on its own and the
-// pieces added at the end.  Here the pieces are partitions of up to
-// part_tokens positions, each carrying (running max m, running sum l,
-// unnormalised value sum), merged by rescaling to a common max.
+// pieces added at the end.  Here a piece is any run of consecutive 16-token
+// tiles of one (sequence, head) pair, carrying (running max m, running sum
+// l, unnormalised value sum); pieces are merged by rescaling to a common max.
 //
-// Mapping to CDNA4.  One workgroup = 4 wave64s = one (sequence, head,
-// partition).  The K (or V) row of one token and head is D*elt bytes
-// contiguous inside its block (256 B for fp16/bf16 D=128), so a token row is
-// covered by LPT = row/16 lanes doing one 16-byte load each, and one
-// global_load_dwordx4 of the wave covers 64/LPT consecutive tokens: fully
-// coalesced 1 KB reads chased through the block table.  A wave processes 16
-// tokens per step (a tile); the four waves take the partition's tiles
-// round-robin.  q.k is 4 packed dot2 instructions per lane (fp16/bf16)
-// followed by a DPP all-reduce over the LPT lanes of the token; each lane
-// group keeps its own online-softmax state and value accumulator (fp32), so
-// the inner loop has no cross-row traffic.  Groups, then waves (through
-// LDS), are merged once at the end.  The table entries a partition needs are
-// fetched once per wave, one per lane, and broadcast with readlane.
-// The next tile's K and V are loaded before the current tile is consumed.
+// Work decomposition (stream-K).  Decode is bound by HBM reads, and context
+// lengths vary, so the batch is treated as one stream of tiles: every
+// (sequence s, head h, tile t) in the order s, h, t gets a global index g in
+// [0, T_total).  The G resident waves (as many as fit on the chip) each take
+// an equal contiguous range [floor(w*T/G), floor((w+1)*T/G)) and walk it
+// without pause across pair boundaries.  A pair that lies inside one range
+// is finished by that wave, which writes the output; a pair cut by range
+// boundaries leaves one fragment per wave involved (at most two per wave),
+// and a small fix-up kernel merges them.  A one-workgroup plan kernel
+// prefix-sums the tile counts, writes every wave's start (s, h, t) and
+// zeroes the outputs of empty sequences.
+//
+// Mapping to CDNA4.  A wave is an independent worker (no LDS, no barriers).
+// The K (or V) row of one token and head is D*elt bytes contiguous inside its
+// block (256 B for fp16/bf16 D=128), so a token row is covered by LPT =
+// row/16 lanes doing one 16-byte load each, and one global_load_dwordx4 of
+// the wave covers 64/LPT consecutive tokens: fully coalesced 1 KB reads
+// chased through the block table (entries fetched with scalar loads), issued
+// non-temporal since every byte is read once.  PA_DECODE_DEPTH tiles are in
+// flight per wave; the issue cursor runs that far ahead of the consume
+// cursor, across pair boundaries.  q.k is 4 packed dot2 instructions per lane
+// (fp16/bf16) followed by a DPP all-reduce over the LPT lanes of the token;
+// each lane group keeps its own online-softmax state and fp32 value
+// accumulator, merged with lane swaps when a pair ends.
 
 #include "pa_device.h"
 #include "pa_internal.h"
 
+#ifndef PA_DECODE_DEPTH
+#define PA_DECODE_DEPTH 2
+#endif
+// 1: stream K/V with non-temporal loads (they are read exactly once).
+#ifndef PA_DECODE_NT
+#define PA_DECODE_NT 1
+#endif
+
 namespace pa {
 
-constexpr int kDecodeWaves = 4;
+constexpr int kDepth = PA_DECODE_DEPTH;
+constexpr int kPlanThreads = 1024;
+
+__device__ __forceinline__ uint4 load16(const char *p) {
+#if PA_DECODE_NT
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *reinterpret_cast<const uint4 *>(p);
+#endif
+}
 
 template <Dt T, int D>
 struct RowShape {
   static constexpr int kEB = EltBytes<T>::value;
-  static constexpr int kRowBytes = D * kEB;      // one token row of one head
-  static constexpr int kLPT = kRowBytes / 16;    // lanes per token row
-  static constexpr int kGroups = kWave / kLPT;   // tokens per wave load
+  static constexpr int kRowBytes = D * kEB;          // one token row of one head
+  static constexpr int kLPT = kRowBytes / 16;        // lanes per token row
+  static constexpr int kGroups = kWave / kLPT;       // tokens per wave load
   static constexpr int kNI = kDecodeTile / kGroups;  // loads per tile
-  static constexpr int kFE = Frag<T>::kElems;    // elements per lane fragment
+  static constexpr int kFE = Frag<T>::kElems;        // elements per lane fragment
   static_assert(kRowBytes % 16 == 0 && kLPT >= 1 && kLPT <= kWave, "row must be whole fragments");
   static_assert(kDecodeTile % kGroups == 0, "tile must be whole wave loads");
   static_assert(kLPT * kFE == D, "fragments must tile the head");
 };
 
 __device__ __forceinline__ int clip_ctx(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
+__device__ __forceinline__ int tiles_of(int n) { return (n + kDecodeTile - 1) / kDecodeTile; }
+
+// Range [g0, g1) of global tiles owned by worker wave w of G.
+__device__ __forceinline__ uint32_t range_begin(uint32_t w, uint32_t total, uint32_t G) {
+  return (uint32_t)(((uint64_t)w * total) / G);
+}
 
 template <Dt T, int D>
 __device__ __forceinline__ void store_out_elem(void *out, int64_t idx, float x) {
@@ -60,90 +94,213 @@ __device__ __forceinline__ void store_out_elem(void *out, int64_t idx, float x) 
   }
 }
 
-template <Dt T, int D, int B>
-__global__ __launch_bounds__(kDecodeWaves *kWave) void decode_partition_kernel(DecodeArgs a) {
-  using R = RowShape<T, D>;
-  const int part = blockIdx.x;
-  const int h = blockIdx.y;
-  const int s = blockIdx.z;
-  const int lane = threadIdx.x % kWave;
-  const int wave = wave_id_uniform();
+// ----------------------------------------------------------------------- plan
 
-  const int n = clip_ctx(a.context_lens[s], a.ctx_cap);
-  const int nparts = (n + a.part_tokens - 1) / a.part_tokens;
-  const int64_t out_row = ((int64_t)s * a.num_heads + h) * D;
-  if (n == 0) {
-    if (part == 0 && threadIdx.x < D) store_out_elem<T, D>(a.out, out_row + threadIdx.x, 0.f);
-    return;
+// One workgroup.  plan[0] = total tiles T, plan[1] = G = min(launched
+// workers, T), and for every worker w < G the (s | h << 16, t) of its first
+// tile at plan[kPlanHeader + 2w].
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a) {
+  __shared__ uint32_t scan[kPlanThreads];
+  const int tid = threadIdx.x;
+  const int S = a.num_seqs;
+  const uint32_t H = (uint32_t)a.num_heads;
+  const int per = (S + kPlanThreads - 1) / kPlanThreads;
+  const int lo = min(S, tid * per), hi = min(S, lo + per);
+  uint32_t mine = 0;
+  for (int s = lo; s < hi; ++s) mine += (uint32_t)tiles_of(clip_ctx(a.context_lens[s], a.ctx_cap)) * H;
+  scan[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive Hillis-Steele scan
+    const uint32_t v = tid >= off ? scan[tid - off] : 0u;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
   }
-  if (part >= nparts) return;
+  const uint32_t total = scan[kPlanThreads - 1];
+  // Never more workers than tiles, so that every worker's range is non-empty.
+  const uint32_t G = total < (uint32_t)a.workers ? total : (uint32_t)a.workers;
+  uint32_t c = scan[tid] - mine;  // tiles before sequence lo
+  if (tid == 0) {
+    a.plan[0] = total;
+    a.plan[1] = G;
+  }
+  for (int s = lo; s < hi; ++s) {
+    const int n = clip_ctx(a.context_lens[s], a.ctx_cap);
+    const uint32_t ts = (uint32_t)tiles_of(n);
+    const uint32_t c_next = c + ts * H;
+    if (ts > 0) {
+      // Workers whose first tile falls in [c, c_next): w in [ceil(c*G/T), ceil(c_next*G/T)).
+      const uint64_t w_lo = ((uint64_t)c * G + total - 1) / total;
+      const uint64_t w_hi = ((uint64_t)c_next * G + total - 1) / total;
+      for (uint64_t w = w_lo; w < w_hi; ++w) {
+        const uint32_t local = range_begin((uint32_t)w, total, G) - c;
+        a.plan[kPlanHeader + 2 * w] = (uint32_t)s | ((local / ts) << 16);
+        a.plan[kPlanHeader + 2 * w + 1] = local % ts;
+      }
+    } else {
+      uint32_t *row = reinterpret_cast<uint32_t *>(a.out) + (int64_t)s * a.out_row_words;
+      for (int i = 0; i < a.out_row_words; ++i) row[i] = 0u;  // +0.0 in every dtype
+    }
+    c = c_next;
+  }
+}
 
-  const int p_begin = part * a.part_tokens;
-  const int p_end = min(n, p_begin + a.part_tokens);
-  const int tile_begin = p_begin / kDecodeTile;
-  const int tile_end = (p_end + kDecodeTile - 1) / kDecodeTile;
-  const int blk_begin = p_begin / B;
-  const int nblk = (p_end + B - 1) / B - blk_begin;  // <= kMaxPartitionBlocks
+// ------------------------------------------------------------ partition pass
+
+// Position of a cursor in the tile stream.  All fields are wave-uniform.
+struct Cursor {
+  int s, h, t;     // sequence, head, tile within the pair
+  int n, nt;       // context length and tiles of sequence s
+  uint32_t g;      // global tile index
+};
+
+// Step to the next tile; crosses to the next head, then to the next
+// non-empty sequence.  Only called while g + 1 < end, so a next tile exists.
+__device__ __forceinline__ void cursor_next(Cursor &c, const DecodeArgs &a) {
+  ++c.g;
+  if (++c.t < c.nt) return;
+  c.t = 0;
+  if (++c.h < a.num_heads) return;
+  c.h = 0;
+  do {
+    ++c.s;
+    c.n = clip_ctx(a.context_lens[c.s], a.ctx_cap);
+    c.nt = tiles_of(c.n);
+  } while (c.nt == 0);
+}
+
+template <Dt T, int D, int B>
+__global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_kernel(DecodeArgs a) {
+  using R = RowShape<T, D>;
+  const int lane = threadIdx.x % kWave;
+  const uint32_t G = a.plan[1];
+  const uint32_t w = blockIdx.x * kDecodeWavesPerGroup + wave_id_uniform();
+  if (w >= G) return;
+  const uint32_t total = a.plan[0];
+  const uint32_t g0 = range_begin(w, total, G), g1 = range_begin(w + 1, total, G);
 
   const int grp = lane / R::kLPT;  // token slot within one wave load
   const int col = lane % R::kLPT;  // 16-byte column within the token row
-
-  // One table entry per lane; broadcast later.
-  const int32_t *table = a.block_tables + (int64_t)s * a.max_blocks;
-  const int32_t my_entry = (lane < nblk) ? table[blk_begin + lane] : -1;
-
-  const char *q_ptr = reinterpret_cast<const char *>(a.q) + out_row * R::kEB + col * 16;
-  const uint4 qf = *reinterpret_cast<const uint4 *>(q_ptr);
-
   const char *kbase = reinterpret_cast<const char *>(a.k_cache);
   const char *vbase = reinterpret_cast<const char *>(a.v_cache);
   const int64_t block_stride = (int64_t)a.num_heads * B * R::kRowBytes;
-  const int64_t lane_off = (int64_t)h * B * R::kRowBytes + col * 16;
 
-  // Loads of one tile.  ok[i]: the token of load i exists (position inside
-  // the partition, table entry inside the pool); masked fragments are zero.
-  auto load_tile = [&](int tile, uint4 *kf, uint4 *vf, bool *ok) {
+  Cursor ic;  // issue cursor
+  {
+    const uint32_t sh = a.plan[kPlanHeader + 2 * w];
+    ic.s = (int)(sh & 0xffffu);
+    ic.h = (int)(sh >> 16);
+    ic.t = (int)a.plan[kPlanHeader + 2 * w + 1];
+    ic.n = clip_ctx(a.context_lens[ic.s], a.ctx_cap);
+    ic.nt = tiles_of(ic.n);
+    ic.g = g0;
+  }
+  Cursor cc = ic;  // consume cursor
+
+  // Table entry of logical block `blk` of sequence s; -1 when outside the pool.
+  auto entry = [&](int s, int blk) -> int32_t {
+    const int32_t e = a.block_tables[(int64_t)s * a.max_blocks + blk];
+    return (e >= 0 && (int64_t)e < a.num_blocks) ? e : -1;
+  };
+
+  // Issue the loads of the tile under the issue cursor into one slot.
+  auto issue = [&](uint4 *kf, uint4 *vf, uint4 &qf, uint32_t &okm) {
+    const bool first = (ic.t == 0) || (ic.g == g0);
+    if (first) {
+      const char *qp = reinterpret_cast<const char *>(a.q) + ((int64_t)ic.s * a.num_heads + ic.h) * R::kRowBytes;
+      qf = *reinterpret_cast<const uint4 *>(qp + col * 16);
+    }
+    const int base = ic.t * kDecodeTile;
+    const int64_t head_off = (int64_t)ic.h * B * R::kRowBytes + col * 16;
+    okm = 0;
 #pragma unroll
     for (int i = 0; i < R::kNI; ++i) {
-      const int pos = tile * kDecodeTile + i * R::kGroups + grp;
+      const int pos = base + i * R::kGroups + grp;
+      // A table entry is read only for a block whose first token is < n,
+      // so the read stays inside the sequence's row.
+      const int pos0 = base + i * R::kGroups;  // first token of this load
       int32_t phys;
-      if constexpr (B >= kDecodeTile) {
-        const int bi = tile * kDecodeTile / B - blk_begin;  // uniform
-        phys = __builtin_amdgcn_readlane(my_entry, bi);
+      if constexpr (B >= R::kGroups) {
+        phys = pos0 < ic.n ? entry(ic.s, pos0 / B) : -1;  // one block for the whole load
       } else {
-        phys = __shfl(my_entry, pos / B - blk_begin, kWave);
+        static_assert(R::kGroups == 2 * B, "a load spans at most two blocks");
+        const int b0 = pos0 / B;
+        const int32_t e0 = pos0 < ic.n ? entry(ic.s, b0) : -1;
+        const int32_t e1 = (b0 + 1) * B < ic.n ? entry(ic.s, b0 + 1) : -1;
+        phys = (grp >= B) ? e1 : e0;
       }
-      ok[i] = (pos < p_end) && (phys >= 0) && ((int64_t)phys < a.num_blocks);
-      const int64_t off = (int64_t)phys * block_stride + lane_off + (int64_t)(pos % B) * R::kRowBytes;
+      const bool ok = (pos < ic.n) && (phys >= 0);
       uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (ok[i]) {
-        kv = *reinterpret_cast<const uint4 *>(kbase + off);
-        vv = *reinterpret_cast<const uint4 *>(vbase + off);
+      if (ok) {
+        const int64_t off = (int64_t)phys * block_stride + head_off + (int64_t)(pos % B) * R::kRowBytes;
+        kv = load16(kbase + off);
+        vv = load16(vbase + off);
       }
       kf[i] = kv;
       vf[i] = vv;
+      okm |= ok ? (1u << i) : 0u;
     }
   };
 
   float m_run = -INFINITY, l_run = 0.f;
   float acc[R::kFE];
+  uint4 qcur = make_uint4(0, 0, 0, 0);
+
+  // Finish the pair under the consume cursor: merge the lane groups, then
+  // write the output (pair inside this range) or a fragment.
+  auto finish = [&]() {
 #pragma unroll
-  for (int e = 0; e < R::kFE; ++e) acc[e] = 0.f;
+    for (int x = R::kLPT; x < kWave; x *= 2) {
+      const float mo = __shfl_xor(m_run, x, kWave);
+      const float lo = __shfl_xor(l_run, x, kWave);
+      const float mn = fmaxf(m_run, mo);
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      const float fa = fast_exp2(m_run - mu), fb = fast_exp2(mo - mu);
+      l_run = l_run * fa + lo * fb;
+#pragma unroll
+      for (int e = 0; e < R::kFE; ++e) acc[e] = acc[e] * fa + __shfl_xor(acc[e], x, kWave) * fb;
+      m_run = mn;
+    }
+    const uint32_t pair_start = cc.g - (uint32_t)cc.t;
+    const uint32_t pair_end = pair_start + (uint32_t)cc.nt;
+    if (pair_start >= g0 && pair_end <= g1) {
+      if (lane < R::kLPT) {
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        float o[R::kFE];
+#pragma unroll
+        for (int e = 0; e < R::kFE; ++e) o[e] = acc[e] * inv;
+        char *op = reinterpret_cast<char *>(a.out) + ((int64_t)cc.s * a.num_heads + cc.h) * R::kRowBytes;
+        *reinterpret_cast<uint4 *>(op + col * 16) = frag_pack<T>(o);
+      }
+    } else {
+      const int slot = pair_start < g0 ? 0 : 1;
+      float *f = a.frags + ((int64_t)w * 2 + slot) * (D + 2);
+      if (lane < R::kLPT) {
+#pragma unroll
+        for (int e = 0; e < R::kFE; ++e) f[col * R::kFE + e] = acc[e];
+      }
+      if (lane == 0) {
+        f[D] = m_run;
+        f[D + 1] = l_run;
+      }
+    }
+  };
 
-  uint4 kc[R::kNI], vc[R::kNI], kn[R::kNI], vn[R::kNI];
-  bool okc[R::kNI], okn[R::kNI];
-  int tile = tile_begin + wave;
-  if (tile < tile_end) load_tile(tile, kc, vc, okc);
-  while (tile < tile_end) {
-    const int next = tile + kDecodeWaves;
-    if (next < tile_end) load_tile(next, kn, vn, okn);
-
+  // Fold one tile into the running state of the pair under the consume cursor.
+  auto consume = [&](const uint4 *kf, const uint4 *vf, const uint4 &qslot, uint32_t okm) {
+    if (cc.t == 0 || cc.g == g0) {
+      qcur = qslot;
+      m_run = -INFINITY;
+      l_run = 0.f;
+#pragma unroll
+      for (int e = 0; e < R::kFE; ++e) acc[e] = 0.f;
+    }
     float sc[R::kNI];
     float mt = -INFINITY;
 #pragma unroll
     for (int i = 0; i < R::kNI; ++i) {
-      float d = group_sum<R::kLPT>(frag_dot<T>(qf, kc[i]));
-      sc[i] = okc[i] ? d * a.scale_log2 : -INFINITY;
+      const float d = group_sum<R::kLPT>(frag_dot<T>(qcur, kf[i]));
+      sc[i] = (okm >> i) & 1u ? d * a.scale_log2 : -INFINITY;
       mt = fmaxf(mt, sc[i]);
     }
     const float m_new = fmaxf(m_run, mt);
@@ -156,98 +313,74 @@ __global__ __launch_bounds__(kDecodeWaves *kWave) void decode_partition_kernel(D
     for (int i = 0; i < R::kNI; ++i) {
       const float p = fast_exp2(sc[i] - m_use);
       l_run += p;
-      frag_axpy<T>(acc, p, vc[i]);
+      frag_axpy<T>(acc, p, vf[i]);
     }
     m_run = m_new;
+    if (cc.t + 1 == cc.nt || cc.g + 1 == g1) finish();
+  };
 
+  uint4 kb[kDepth][R::kNI], vb[kDepth][R::kNI], qb[kDepth];
+  uint32_t okb[kDepth];
+  // Prime the pipeline.
 #pragma unroll
-    for (int i = 0; i < R::kNI; ++i) {
-      kc[i] = kn[i];
-      vc[i] = vn[i];
-      okc[i] = okn[i];
+  for (int d = 0; d < kDepth; ++d) {
+    if (ic.g < g1) {
+      issue(kb[d], vb[d], qb[d], okb[d]);
+      if (ic.g + 1 < g1) cursor_next(ic, a); else ic.g = g1;
     }
-    tile = next;
   }
-
-  // Merge the lane groups of the wave (each saw its own tokens).
+  // Steady state: consume slot d, then refill it with the tile kDepth ahead.
+  while (cc.g < g1) {
 #pragma unroll
-  for (int x = R::kLPT; x < kWave; x *= 2) {
-    const float mo = __shfl_xor(m_run, x, kWave);
-    const float lo = __shfl_xor(l_run, x, kWave);
-    const float mn = fmaxf(m_run, mo);
-    const float mu = (mn == -INFINITY) ? 0.f : mn;
-    const float fa = fast_exp2(m_run - mu), fb = fast_exp2(mo - mu);
-    l_run = l_run * fa + lo * fb;
-#pragma unroll
-    for (int e = 0; e < R::kFE; ++e) acc[e] = acc[e] * fa + __shfl_xor(acc[e], x, kWave) * fb;
-    m_run = mn;
-  }
-
-  // Merge the waves through LDS.
-  __shared__ float sh_m[kDecodeWaves], sh_l[kDecodeWaves];
-  __shared__ float sh_acc[kDecodeWaves][D];
-  if (lane < R::kLPT) {
-#pragma unroll
-    for (int e = 0; e < R::kFE; ++e) sh_acc[wave][col * R::kFE + e] = acc[e];
-  }
-  if (lane == 0) {
-    sh_m[wave] = m_run;
-    sh_l[wave] = l_run;
-  }
-  __syncthreads();
-  if (threadIdx.x < D) {
-    const int d = threadIdx.x;
-    float M = sh_m[0];
-#pragma unroll
-    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, sh_m[w]);
-    const float mu = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f, A = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      const float f = fast_exp2(sh_m[w] - mu);
-      L += sh_l[w] * f;
-      A += sh_acc[w][d] * f;
-    }
-    if (nparts == 1) {
-      store_out_elem<T, D>(a.out, out_row + d, L > 0.f ? A / L : 0.f);
-    } else {
-      const int64_t slot = ((int64_t)s * a.num_heads + h) * a.max_parts + part;
-      a.ws_acc[slot * D + d] = A;
-      if (d == 0) {
-        a.ws_ml[2 * slot] = M;
-        a.ws_ml[2 * slot + 1] = L;
+    for (int d = 0; d < kDepth; ++d) {
+      if (cc.g < g1) {
+        consume(kb[d], vb[d], qb[d], okb[d]);
+        if (cc.g + 1 < g1) cursor_next(cc, a); else cc.g = g1;
+        if (ic.g < g1) {
+          issue(kb[d], vb[d], qb[d], okb[d]);
+          if (ic.g + 1 < g1) cursor_next(ic, a); else ic.g = g1;
+        }
       }
     }
   }
 }
 
-// Merge the partials of sequences with two or more partitions.
+// Merge the fragments of every pair cut by range boundaries.  Worker wave w
+// handles the pair holding its first tile when that pair started before its
+// range and ends inside it (so every fragment of the pair exists).
 template <Dt T, int D>
-__global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a) {
-  const int h = blockIdx.x;
-  const int s = blockIdx.y;
-  const int lane = threadIdx.x;
-  const int n = clip_ctx(a.context_lens[s], a.ctx_cap);
-  const int nparts = (n + a.part_tokens - 1) / a.part_tokens;
-  if (nparts <= 1) return;
-  const int64_t base = ((int64_t)s * a.num_heads + h) * a.max_parts;
+__global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_reduce_kernel(DecodeArgs a) {
+  // Every worker wave v that the loop below visits has a non-empty range
+  // (the plan never uses more workers than tiles) and wrote its fragment.
+  const int lane = threadIdx.x % kWave;
+  const uint32_t G = a.plan[1];
+  const uint32_t w = blockIdx.x * kDecodeWavesPerGroup + wave_id_uniform();
+  if (w >= G) return;
+  const uint32_t total = a.plan[0];
+  const uint32_t g0 = range_begin(w, total, G), g1 = range_begin(w + 1, total, G);
+  const uint32_t sh = a.plan[kPlanHeader + 2 * w];
+  const int s = (int)(sh & 0xffffu), h = (int)(sh >> 16);
+  const uint32_t t = a.plan[kPlanHeader + 2 * w + 1];
+  if (t == 0) return;  // the pair starts at g0: not cut at the front of this range
+  const uint32_t nt = (uint32_t)tiles_of(clip_ctx(a.context_lens[s], a.ctx_cap));
+  const uint32_t pair_start = g0 - t;
+  if (pair_start + nt > g1) return;  // continues past this range: a later worker merges it
+  // First worker holding the pair: the last w' with range_begin(w') <= pair_start.
+  const uint32_t wa = (uint32_t)((((uint64_t)pair_start + 1) * G + total - 1) / total) - 1;
 
+  auto frag = [&](uint32_t v) -> const float * {
+    return a.frags + ((int64_t)v * 2 + (v == wa ? 1 : 0)) * (D + 2);
+  };
   float M = -INFINITY;
-  for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, a.ws_ml[2 * (base + p)]);
-#pragma unroll
-  for (int x = 1; x < kWave; x *= 2) M = fmaxf(M, __shfl_xor(M, x, kWave));
+  for (uint32_t v = wa; v <= w; ++v) M = fmaxf(M, frag(v)[D]);
   const float mu = (M == -INFINITY) ? 0.f : M;
   float L = 0.f;
-  for (int p = lane; p < nparts; p += kWave) L += a.ws_ml[2 * (base + p) + 1] * fast_exp2(a.ws_ml[2 * (base + p)] - mu);
-#pragma unroll
-  for (int x = 1; x < kWave; x *= 2) L += __shfl_xor(L, x, kWave);
+  for (uint32_t v = wa; v <= w; ++v) L += frag(v)[D + 1] * fast_exp2(frag(v)[D] - mu);
   const float inv = L > 0.f ? 1.f / L : 0.f;
-
   const int64_t out_row = ((int64_t)s * a.num_heads + h) * D;
-#pragma unroll
   for (int d = lane; d < D; d += kWave) {
     float A = 0.f;
-    for (int p = 0; p < nparts; ++p) A += a.ws_acc[(base + p) * D + d] * fast_exp2(a.ws_ml[2 * (base + p)] - mu);
+    for (uint32_t v = wa; v <= w; ++v) A += frag(v)[d] * fast_exp2(frag(v)[D] - mu);
     store_out_elem<T, D>(a.out, out_row + d, A * inv);
   }
 }
@@ -255,21 +388,47 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a) {
 // ------------------------------------------------------------------ dispatch
 
 template <Dt T, int D, int B>
+static int waves_per_cu() {
+  static const int v = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partition_kernel<T, D, B>,
+                                                     kDecodeWavesPerGroup * kWave, 0) != hipSuccess ||
+        nb < 1)
+      nb = 1;
+    return nb * kDecodeWavesPerGroup;
+  }();
+  return v;
+}
+
+template <Dt T, int D, int B>
 static hipError_t launch_part(const DecodeArgs &a, hipStream_t st) {
-  dim3 grid(a.max_parts, a.num_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, B>), grid, dim3(kDecodeWaves * kWave), 0, st, a);
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned groups = (unsigned)((a.workers + kDecodeWavesPerGroup - 1) / kDecodeWavesPerGroup);
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, B>), dim3(groups), dim3(kDecodeWavesPerGroup * kWave), 0, st,
+                     a);
   return hipGetLastError();
 }
 
+#define PA_DISPATCH_B(B, FN, ...)                  \
+  switch (B) {                                     \
+    case 4: return FN<T, D, 4>(__VA_ARGS__);       \
+    case 8: return FN<T, D, 8>(__VA_ARGS__);       \
+    case 16: return FN<T, D, 16>(__VA_ARGS__);     \
+    case 32: return FN<T, D, 32>(__VA_ARGS__);     \
+  }
+
 template <Dt T, int D>
 static hipError_t launch_part_b(const DecodeArgs &a, int B, hipStream_t st) {
-  switch (B) {
-    case 4: return launch_part<T, D, 4>(a, st);
-    case 8: return launch_part<T, D, 8>(a, st);
-    case 16: return launch_part<T, D, 16>(a, st);
-    case 32: return launch_part<T, D, 32>(a, st);
-  }
+  PA_DISPATCH_B(B, launch_part, a, st)
   return hipErrorInvalidValue;
+}
+
+template <Dt T, int D>
+static int waves_b(int B) {
+  PA_DISPATCH_B(B, waves_per_cu)
+  return 0;
 }
 
 template <Dt T>
@@ -281,11 +440,29 @@ static hipError_t launch_part_d(const DecodeArgs &a, int D, int B, hipStream_t s
   return hipErrorInvalidValue;
 }
 
+template <Dt T>
+static int waves_d(int D, int B) {
+  switch (D) {
+    case 64: return waves_b<T, 64>(B);
+    case 128: return waves_b<T, 128>(B);
+  }
+  return 0;
+}
+
 bool decode_supported(int dtype, int head_dim, int block_size) {
   const bool dt = dtype >= 0 && dtype <= 2;
   const bool d = head_dim == 64 || head_dim == 128;
   const bool b = block_size == 4 || block_size == 8 || block_size == 16 || block_size == 32;
   return dt && d && b;
+}
+
+int decode_waves_per_cu(int dtype, int head_dim, int block_size) {
+  switch (static_cast<Dt>(dtype)) {
+    case Dt::F32: return waves_d<Dt::F32>(head_dim, block_size);
+    case Dt::F16: return waves_d<Dt::F16>(head_dim, block_size);
+    case Dt::BF16: return waves_d<Dt::BF16>(head_dim, block_size);
+  }
+  return 0;
 }
 
 hipError_t launch_decode_partitions(const DecodeArgs &a, int dtype, int head_dim, int block_size,
@@ -301,17 +478,21 @@ hipError_t launch_decode_partitions(const DecodeArgs &a, int dtype, int head_dim
 
 template <Dt T>
 static hipError_t launch_red(const DecodeArgs &a, int D, hipStream_t st) {
-  dim3 grid(a.num_heads, a.num_seqs);
+  const dim3 grid((unsigned)((a.workers + kDecodeWavesPerGroup - 1) / kDecodeWavesPerGroup));
   switch (D) {
-    case 64: hipLaunchKernelGGL((decode_reduce_kernel<T, 64>), grid, dim3(kWave), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((decode_reduce_kernel<T, 128>), grid, dim3(kWave), 0, st, a); break;
+    case 64:
+      hipLaunchKernelGGL((decode_reduce_kernel<T, 64>), grid, dim3(kDecodeWavesPerGroup * kWave), 0, st, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL((decode_reduce_kernel<T, 128>), grid, dim3(kDecodeWavesPerGroup * kWave), 0, st, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_decode_reduce(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream) {
-  if (a.num_seqs == 0 || a.max_parts <= 1) return hipSuccess;
+  if (a.num_seqs == 0 || a.workers <= 1) return hipSuccess;
   switch (static_cast<Dt>(dtype)) {
     case Dt::F32: return launch_red<Dt::F32>(a, head_dim, stream);
     case Dt::F16: return launch_red<Dt::F16>(a, head_dim, stream);

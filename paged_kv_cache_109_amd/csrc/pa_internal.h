@@ -9,11 +9,11 @@ namespace pa {
 
 enum class Dt : int;
 
-// Arguments of the decode partition pass.  Pointers are device pointers.
+// Arguments of the decode passes.  Pointers are device pointers.
 struct DecodeArgs {
   void *out;            // [S][H][D] dtype
-  float *ws_ml;         // [S][H][max_parts][2]   (m in log2 units, l)
-  float *ws_acc;        // [S][H][max_parts][D]
+  uint32_t *plan;       // [kPlanHeader + 2*workers]: total tiles, workers used, per-worker start
+  float *frags;         // [workers][2][D + 2]: fragment value sums, then m (log2 units), l
   const void *q;        // [S][H][D]
   const void *k_cache;  // [N][H][B][D]
   const void *v_cache;
@@ -23,17 +23,23 @@ struct DecodeArgs {
   int32_t num_seqs;
   int32_t max_blocks;
   int32_t num_heads;
-  int32_t ctx_cap;      // context lengths are clipped to [0, ctx_cap]
-  int32_t part_tokens;  // tokens per partition
-  int32_t max_parts;    // ceil(ctx_cap / part_tokens)
-  float scale_log2;     // softmax scale * log2(e)
+  int32_t ctx_cap;        // context lengths are clipped to [0, ctx_cap]
+  int32_t workers;        // worker waves launched (the split of the tile stream)
+  int32_t out_row_words;  // 32-bit words of one sequence's output rows (H*D*elt/4)
+  float scale_log2;       // softmax scale * log2(e)
 };
 
-// Tokens a decode wave processes per step; partitions are whole tiles.
+// 32-bit words before the per-worker starts in the plan.
+constexpr int kPlanHeader = 4;
+// Tokens a decode wave processes per step (one tile).
 constexpr int kDecodeTile = 16;
-// Most table entries one partition may span (one per lane of a wave).
-constexpr int kMaxPartitionBlocks = 64;
+// Independent worker waves packed into one workgroup.
+constexpr int kDecodeWavesPerGroup = 4;
+// Upper bound of resident waves per CU used to size workspaces.
+constexpr int kMaxWavesPerCu = 32;
 
+// Resident worker waves per CU of the decode instantiation (0 if unsupported).
+int decode_waves_per_cu(int dtype, int head_dim, int block_size);
 bool decode_supported(int dtype, int head_dim, int block_size);
 hipError_t launch_decode_partitions(const DecodeArgs &a, int dtype, int head_dim, int block_size,
                                     hipStream_t stream);

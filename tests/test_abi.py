@@ -59,7 +59,7 @@ def decode(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(dt=7), 1), (dict(H=0), 1), (dict(N=0), 1), (dict(M=0), 1), (dict(max_ctx=-1), 1),
     (dict(D=96), 2), (dict(Bs=12), 2), (dict(Bs=64), 2), (dict(k=None), 1), (dict(q=FAKE + 8), 1),
-    (dict(part=24), 1), (dict(part=16 * 64 + 16), 1), (dict(scale=float("nan")), 1),
+    (dict(part=-1), 1), (dict(scale=float("nan")), 1),
     (dict(max_ctx=2048, M=128), 3), (dict(max_ctx=2048, M=128, ws=FAKE, ws_bytes=100), 3), (dict(S=70000), 2),
 ])
 def test_decode_rejects_bad_arguments(over, status):
@@ -69,11 +69,12 @@ def test_decode_rejects_bad_arguments(over, status):
 
 
 def test_workspace_sizing():
-    assert pa.decode_workspace_bytes(64, 40, 128, 512, 16) == 0
-    P = pa.decode_partition_size(2048, 16)
-    parts = -(-2048 // P)
-    assert pa.decode_workspace_bytes(64, 40, 128, 2048, 16) == 64 * 40 * parts * (128 + 2) * 4
-    assert pa.decode_workspace_bytes(3, 2, 64, 100, 16, 16) == 3 * 2 * 7 * 66 * 4
+    def ws(workers, D=128):
+        return -(-(4 + 2 * workers) * 4 // 256) * 256 + workers * 2 * (D + 2) * 4
+    assert pa.decode_workspace_bytes(64, 40, 128, 2048, 16, 300) == ws(300)
+    assert pa.decode_workspace_bytes(3, 2, 64, 100, 16, 7) == ws(7, 64)
+    assert pa.decode_workspace_bytes(0, 2, 64, 100, 16) == 0
+    assert pa.decode_workspace_bytes(5, 2, 64, 100, 16, 0) >= ws(256 * 4, 64)   # default: device bound
 
 
 def test_reshape_rejects_bad_arguments():

@@ -17,12 +17,12 @@ from gpu_util import DeviceCase, check_attention, say
 pytestmark = pytest.mark.gpu
 
 
-def gpu_decode(dc: DeviceCase, partition_size: int = 0):
+def gpu_decode(dc: DeviceCase, split_workers: int = 0):
     c = dc.case
     say(f"  decode {c.name}: S={c.num_seqs} H={c.num_heads} D={c.head_dim} B={c.block_size} {c.dtype} "
-        f"max_ctx={c.max_context_len} partition={partition_size}")
+        f"max_ctx={c.max_context_len} split_workers={split_workers}")
     pa.paged_attention_decode(dc.out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
-                              c.max_context_len, c.scale, partition_size=partition_size)
+                              c.max_context_len, c.scale, split_workers=split_workers)
     torch.cuda.synchronize()
     return dc.out
 
@@ -51,16 +51,25 @@ def test_decode_shapes(dtype, D, B):
                            max_blocks_per_seq=W.blocks_needed(max(LENS), B) + 2, poison_unused=True, pad_entry=-1)
     dc = DeviceCase(c)
     ref = ref_decode(c)
-    for part in (0, max(16, B), min(64 * B, 1024)):
-        check_attention(gpu_decode(dc, part), ref, dtype, f"{c.name} D={D} B={B} {dtype} part={part}")
+    for workers in (0, 1, 7, 97):
+        check_attention(gpu_decode(dc, workers), ref, dtype, f"{c.name} D={D} B={B} {dtype} workers={workers}")
 
 
-@pytest.mark.parametrize("part", [16, 32, 48, 128, 256, 512, 1024])
-def test_partition_size_does_not_change_the_result(part):
+@pytest.mark.parametrize("workers", [1, 2, 3, 5, 16, 61, 64, 255, 1000, 4096, 0])
+def test_split_points_do_not_change_the_result(workers):
+    """The batch's tile stream cut among 1..all worker waves: every cut
+    pattern (pairs finished whole, cut once, cut across many workers, more
+    workers than tiles) must give the oracle's result."""
     c = W.make_decode_case(6, 4, 128, 16, "f16", [1, 47, 300, 1024, 1500, 2048], seed=3,
                            max_blocks_per_seq=128)
     dc = DeviceCase(c)
-    check_attention(gpu_decode(dc, part), ref_decode(c), "f16", f"partition {part}")
+    check_attention(gpu_decode(dc, workers), ref_decode(c), "f16", f"workers {workers}")
+
+
+def test_more_workers_than_tiles():
+    c = W.make_decode_case(3, 2, 64, 16, "bf16", [1, 20, 0], seed=9, max_blocks_per_seq=2)
+    dc = DeviceCase(c)
+    check_attention(gpu_decode(dc, 50), ref_decode(c), "bf16", "tiny")
 
 
 def test_permuting_physical_blocks_is_bit_identical_on_gpu():
@@ -108,13 +117,13 @@ def test_out_of_pool_table_entries_are_ignored_not_read():
 def test_workspace_checks_leave_output_untouched():
     c = W.make_decode_case(2, 2, 128, 16, "f16", [600, 1200], seed=7, max_blocks_per_seq=80)
     dc = DeviceCase(c)
-    need = pa.decode_workspace_bytes(2, 2, 128, c.max_context_len, 16)
+    need = pa.decode_workspace_bytes(2, 2, 128, c.max_context_len, 16, 8)
     assert need > 0
     dc.out.fill_(7.0)
     small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
     with pytest.raises(pa.PagedAttnError) as e:
         pa.paged_attention_decode(dc.out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
-                                  c.max_context_len, c.scale, workspace=small)
+                                  c.max_context_len, c.scale, workspace=small, split_workers=8)
     assert e.value.status == 3
     torch.cuda.synchronize()
     assert (dc.out == 7.0).all()
