@@ -21,7 +21,9 @@
 // boundaries leaves one fragment per wave involved (at most two per wave),
 // and a small fix-up kernel merges them.  A one-workgroup plan kernel
 // prefix-sums the tile counts, writes every wave's start (s, h, t) and
-// zeroes the outputs of empty sequences.
+// zeroes the outputs of empty sequences; for batches of up to 1024
+// sequences the worker waves do that themselves (each reads all lengths),
+// which saves a launch.
 //
 // Mapping to CDNA4.  A wave is an independent worker (no LDS, no barriers).
 // The K (or V) row of one token and head is D*elt bytes contiguous inside its
@@ -40,7 +42,7 @@
 #include "pa_internal.h"
 
 #ifndef PA_DECODE_DEPTH
-#define PA_DECODE_DEPTH 2
+#define PA_DECODE_DEPTH 3
 #endif
 // 1: stream K/V with non-temporal loads (they are read exactly once).
 #ifndef PA_DECODE_NT
@@ -51,6 +53,8 @@ namespace pa {
 
 constexpr int kDepth = PA_DECODE_DEPTH;
 constexpr int kPlanThreads = 1024;
+// Largest batch whose worker waves plan for themselves (16 chunks of 64).
+constexpr int kSelfPlanSeqs = 1024;
 
 __device__ __forceinline__ uint4 load16(const char *p) {
 #if PA_DECODE_NT
@@ -96,9 +100,11 @@ __device__ __forceinline__ void store_out_elem(void *out, int64_t idx, float x) 
 
 // ----------------------------------------------------------------------- plan
 
-// One workgroup.  plan[0] = total tiles T, plan[1] = G = min(launched
-// workers, T), and for every worker w < G the (s | h << 16, t) of its first
-// tile at plan[kPlanHeader + 2w].
+// Plan for batches of more than kSelfPlanSeqs sequences (smaller batches are
+// planned by the worker waves themselves, see self_plan).  One workgroup.
+// plan[0] = total tiles T, plan[1] = G = min(launched workers, T), and for
+// every worker w < G the (s | h << 16, t) of its first tile at
+// plan[kPlanHeader + 2w]; zeroes the outputs of empty sequences.
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a) {
   __shared__ uint32_t scan[kPlanThreads];
   const int tid = threadIdx.x;
@@ -164,19 +170,114 @@ __device__ __forceinline__ void cursor_next(Cursor &c, const DecodeArgs &a) {
   c.h = 0;
   do {
     ++c.s;
-    c.n = clip_ctx(a.context_lens[c.s], a.ctx_cap);
+    c.n = clip_ctx(load_uniform(a.context_lens, c.s), a.ctx_cap);
     c.nt = tiles_of(c.n);
   } while (c.nt == 0);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Batches of at most kSelfPlanSeqs sequences: every worker wave reads all
+// context lengths (one chunk of 64 per VGPR, all loads issued at once),
+// prefix-sums the tile counts across lanes, and finds the (s, h, t) of its
+// first tile itself -- no plan launch.  Wave 0 also publishes T and G in
+// plan[0..1]; every worker stores its start for the fix-up, and zeroes the
+// outputs of the empty sequences s with s % G == w.  Returns false if the
+// wave has no work.
+__device__ __forceinline__ bool self_plan(const DecodeArgs &a, uint32_t w, uint32_t &total, uint32_t &G,
+                                          int &s0, int &h0, int &t0) {
+  constexpr int kChunks = kSelfPlanSeqs / kWave;
+  const int lane = threadIdx.x % kWave;
+  const uint32_t H = (uint32_t)a.num_heads;
+  const int S = a.num_seqs;
+  int32_t raw[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) raw[c] = a.context_lens[min(c * kWave + lane, S - 1)];
+  uint32_t tiles[kChunks];
+  total = 0;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    tiles[c] = c * kWave + lane < S ? (uint32_t)tiles_of(clip_ctx(raw[c], a.ctx_cap)) : 0u;
+    uint32_t x = tiles[c] * H;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off, kWave);
+    total += __builtin_amdgcn_readfirstlane(x);
+  }
+  G = total < (uint32_t)a.workers ? total : (uint32_t)a.workers;
+  if (w == 0 && lane == 0) {
+    a.plan[0] = total;
+    a.plan[1] = G;
+  }
+  // Zero the rows of empty sequences, each row by one whole wave.
+  const uint32_t zero_waves = G > 0 ? G : 1u;
+  if (w < zero_waves) {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int s = c * kWave + lane;
+      uint64_t todo = __builtin_amdgcn_ballot_w64(s < S && tiles[c] == 0 && (uint32_t)s % zero_waves == w);
+      while (todo) {
+        const int l = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        uint4 *row = reinterpret_cast<uint4 *>(reinterpret_cast<uint32_t *>(a.out) +
+                                               (int64_t)(c * kWave + l) * a.out_row_words);
+        for (int i = lane; i < a.out_row_words / 4; i += kWave) row[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  if (w >= G) return false;
+  const uint32_t g0 = range_begin(w, total, G);
+  uint32_t before = 0;  // tiles of the chunks already passed
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const uint32_t v = tiles[c] * H;
+    const uint32_t incl = before + wave_inclusive_scan(v);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > g0);
+    if (hit != 0) {
+      const int l = __builtin_ctzll(hit);  // first lane whose range passes g0
+      const uint32_t ts = __builtin_amdgcn_readlane(tiles[c], l);
+      const uint32_t start = __builtin_amdgcn_readlane(incl - v, l);
+      const uint32_t local = g0 - start;
+      s0 = c * kWave + l;
+      h0 = (int)(local / ts);
+      t0 = (int)(local % ts);
+      if (lane == 0) {
+        a.plan[kPlanHeader + 2 * w] = (uint32_t)s0 | ((uint32_t)h0 << 16);
+        a.plan[kPlanHeader + 2 * w + 1] = (uint32_t)t0;
+      }
+      return true;
+    }
+    before = __builtin_amdgcn_readlane(incl, kWave - 1);
+  }
+  return false;  // not reached: g0 < total
 }
 
 template <Dt T, int D, int B>
 __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_kernel(DecodeArgs a) {
   using R = RowShape<T, D>;
   const int lane = threadIdx.x % kWave;
-  const uint32_t G = a.plan[1];
   const uint32_t w = blockIdx.x * kDecodeWavesPerGroup + wave_id_uniform();
-  if (w >= G) return;
-  const uint32_t total = a.plan[0];
+  uint32_t G, total;
+  Cursor ic;  // issue cursor
+  if (a.num_seqs <= kSelfPlanSeqs) {
+    if (!self_plan(a, w, total, G, ic.s, ic.h, ic.t)) return;
+  } else {
+    G = load_uniform(a.plan, 1);
+    if (w >= G) return;
+    total = load_uniform(a.plan, 0);
+    const uint32_t sh = load_uniform(a.plan, kPlanHeader + 2 * w);
+    ic.s = (int)(sh & 0xffffu);
+    ic.h = (int)(sh >> 16);
+    ic.t = (int)load_uniform(a.plan, kPlanHeader + 2 * w + 1);
+  }
   const uint32_t g0 = range_begin(w, total, G), g1 = range_begin(w + 1, total, G);
 
   const int grp = lane / R::kLPT;  // token slot within one wave load
@@ -185,59 +286,56 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_
   const char *vbase = reinterpret_cast<const char *>(a.v_cache);
   const int64_t block_stride = (int64_t)a.num_heads * B * R::kRowBytes;
 
-  Cursor ic;  // issue cursor
-  {
-    const uint32_t sh = a.plan[kPlanHeader + 2 * w];
-    ic.s = (int)(sh & 0xffffu);
-    ic.h = (int)(sh >> 16);
-    ic.t = (int)a.plan[kPlanHeader + 2 * w + 1];
-    ic.n = clip_ctx(a.context_lens[ic.s], a.ctx_cap);
-    ic.nt = tiles_of(ic.n);
-    ic.g = g0;
-  }
+  ic.n = clip_ctx(load_uniform(a.context_lens, ic.s), a.ctx_cap);
+  ic.nt = tiles_of(ic.n);
+  ic.g = g0;
   Cursor cc = ic;  // consume cursor
 
   // Table entry of logical block `blk` of sequence s; -1 when outside the pool.
   auto entry = [&](int s, int blk) -> int32_t {
-    const int32_t e = a.block_tables[(int64_t)s * a.max_blocks + blk];
+    const int32_t e = load_uniform(a.block_tables, (int64_t)s * a.max_blocks + blk);
     return (e >= 0 && (int64_t)e < a.num_blocks) ? e : -1;
   };
 
-  // Issue the loads of the tile under the issue cursor into one slot.
-  auto issue = [&](uint4 *kf, uint4 *vf, uint4 &qf, uint32_t &okm) {
-    const bool first = (ic.t == 0) || (ic.g == g0);
-    if (first) {
-      const char *qp = reinterpret_cast<const char *>(a.q) + ((int64_t)ic.s * a.num_heads + ic.h) * R::kRowBytes;
-      qf = *reinterpret_cast<const uint4 *>(qp + col * 16);
-    }
+  // Issue the loads of one tile into a slot: q of its pair, then 4 K and 4 V
+  // fragments (for fp16/bf16 D=128).  Every call issues the same loads,
+  // whether or not `live` (the issue cursor inside the range) and whatever
+  // the mask, so the compiler can count outstanding loads exactly and wait
+  // only for the slot being consumed.  Masked and dead loads read row 0 of
+  // block 0 -- always inside the pool -- and are discarded on consumption.
+  auto issue = [&](uint4 *kf, uint4 *vf, uint4 &qf, uint32_t &okm, bool live) {
+    const int s = live ? ic.s : 0, h = live ? ic.h : 0;
+    const char *qp = reinterpret_cast<const char *>(a.q) + ((int64_t)s * a.num_heads + h) * R::kRowBytes;
+    qf = *reinterpret_cast<const uint4 *>(qp + col * 16);
     const int base = ic.t * kDecodeTile;
     const int64_t head_off = (int64_t)ic.h * B * R::kRowBytes + col * 16;
+    // A table entry is read only for a block whose first token is < n, so the
+    // read stays inside the sequence's row.  With B >= 16 one entry covers
+    // the whole tile (base < n always holds for a live tile).
+    int32_t tile_phys = -1;
+    if constexpr (B >= kDecodeTile) tile_phys = live ? entry(ic.s, base / B) : -1;
     okm = 0;
 #pragma unroll
     for (int i = 0; i < R::kNI; ++i) {
       const int pos = base + i * R::kGroups + grp;
-      // A table entry is read only for a block whose first token is < n,
-      // so the read stays inside the sequence's row.
       const int pos0 = base + i * R::kGroups;  // first token of this load
       int32_t phys;
-      if constexpr (B >= R::kGroups) {
-        phys = pos0 < ic.n ? entry(ic.s, pos0 / B) : -1;  // one block for the whole load
+      if constexpr (B >= kDecodeTile) {
+        phys = tile_phys;
+      } else if constexpr (B >= R::kGroups) {
+        phys = (live && pos0 < ic.n) ? entry(ic.s, pos0 / B) : -1;  // one block for the whole load
       } else {
         static_assert(R::kGroups == 2 * B, "a load spans at most two blocks");
         const int b0 = pos0 / B;
-        const int32_t e0 = pos0 < ic.n ? entry(ic.s, b0) : -1;
-        const int32_t e1 = (b0 + 1) * B < ic.n ? entry(ic.s, b0 + 1) : -1;
+        const int32_t e0 = (live && pos0 < ic.n) ? entry(ic.s, b0) : -1;
+        const int32_t e1 = (live && (b0 + 1) * B < ic.n) ? entry(ic.s, b0 + 1) : -1;
         phys = (grp >= B) ? e1 : e0;
       }
-      const bool ok = (pos < ic.n) && (phys >= 0);
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (ok) {
-        const int64_t off = (int64_t)phys * block_stride + head_off + (int64_t)(pos % B) * R::kRowBytes;
-        kv = load16(kbase + off);
-        vv = load16(vbase + off);
-      }
-      kf[i] = kv;
-      vf[i] = vv;
+      const bool ok = live && (pos < ic.n) && (phys >= 0);
+      const int64_t off =
+          ok ? (int64_t)phys * block_stride + head_off + (int64_t)(pos % B) * R::kRowBytes : (int64_t)col * 16;
+      kf[i] = load16(kbase + off);
+      vf[i] = load16(vbase + off);
       okm |= ok ? (1u << i) : 0u;
     }
   };
@@ -287,13 +385,21 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_
   };
 
   // Fold one tile into the running state of the pair under the consume cursor.
-  auto consume = [&](const uint4 *kf, const uint4 *vf, const uint4 &qslot, uint32_t okm) {
+  constexpr uint32_t kAll = (1u << R::kNI) - 1u;
+  auto consume = [&](const uint4 *kf, uint4 *vf, const uint4 &qslot, uint32_t okm) {
     if (cc.t == 0 || cc.g == g0) {
       qcur = qslot;
       m_run = -INFINITY;
       l_run = 0.f;
 #pragma unroll
       for (int e = 0; e < R::kFE; ++e) acc[e] = 0.f;
+    }
+    // Masked fragments hold whatever the dummy row holds: zero their values
+    // (their weights are 0, but 0 * NaN is not).  Rare: partial tiles only.
+    if (__builtin_amdgcn_ballot_w64(okm != kAll) != 0) {
+#pragma unroll
+      for (int i = 0; i < R::kNI; ++i)
+        if (!((okm >> i) & 1u)) vf[i] = make_uint4(0, 0, 0, 0);
     }
     float sc[R::kNI];
     float mt = -INFINITY;
@@ -319,28 +425,31 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_
     if (cc.t + 1 == cc.nt || cc.g + 1 == g1) finish();
   };
 
+  // Software pipeline over the wave's L tiles with kDepth slots.  Every loop
+  // step consumes slot d (if a tile is left) and refills it with the tile
+  // kDepth ahead, or with dummy loads past the end.
+  const uint32_t L = g1 - g0;
+  uint32_t issued = 0;
   uint4 kb[kDepth][R::kNI], vb[kDepth][R::kNI], qb[kDepth];
   uint32_t okb[kDepth];
-  // Prime the pipeline.
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d) {
-    if (ic.g < g1) {
-      issue(kb[d], vb[d], qb[d], okb[d]);
-      if (ic.g + 1 < g1) cursor_next(ic, a); else ic.g = g1;
+  auto refill = [&](int d) {
+    const bool live = issued < L;
+    issue(kb[d], vb[d], qb[d], okb[d], live);
+    if (live) {
+      ++issued;
+      if (issued < L) cursor_next(ic, a);
     }
-  }
-  // Steady state: consume slot d, then refill it with the tile kDepth ahead.
-  while (cc.g < g1) {
+  };
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) refill(d);
+  for (uint32_t it = 0; it < L; it += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
-      if (cc.g < g1) {
+      if (it + d < L) {
         consume(kb[d], vb[d], qb[d], okb[d]);
-        if (cc.g + 1 < g1) cursor_next(cc, a); else cc.g = g1;
-        if (ic.g < g1) {
-          issue(kb[d], vb[d], qb[d], okb[d]);
-          if (ic.g + 1 < g1) cursor_next(ic, a); else ic.g = g1;
-        }
+        if (it + d + 1 < L) cursor_next(cc, a);
       }
+      refill(d);
     }
   }
 }
@@ -402,9 +511,11 @@ static int waves_per_cu() {
 
 template <Dt T, int D, int B>
 static hipError_t launch_part(const DecodeArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (a.num_seqs > kSelfPlanSeqs) {
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const unsigned groups = (unsigned)((a.workers + kDecodeWavesPerGroup - 1) / kDecodeWavesPerGroup);
   hipLaunchKernelGGL((decode_partition_kernel<T, D, B>), dim3(groups), dim3(kDecodeWavesPerGroup * kWave), 0, st,
                      a);

@@ -139,6 +139,15 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Read-only kernel input seen through the constant address space: a load at
+// a wave-uniform index becomes a scalar (SMEM) load, counted on lgkmcnt, so
+// it never waits behind the vector loads in flight.  Only for memory the
+// calling kernel does not write.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T *p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T *)p)[i];
+}
+
 __device__ __forceinline__ int wave_id_uniform() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 }
