@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak
 METRIC = "paged decode attn tokens/s + effective KV GB/s (% HBM peak), OPT-13B shapes"
 
 
@@ -38,7 +39,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="opt13b_b64", choices=["opt13b_b64", "large_batch_b256"])
+    ap.add_argument("--workload", default="opt13b_b64", choices=["opt13b_b64", "large_batch_b256", "chunked_prefill"])
     ap.add_argument("--replicas", type=int, default=2,
                     help="copies of the KV pool used in turn, so no step finds the last one's data in cache")
     ap.add_argument("--split-workers", type=int, default=0,
@@ -80,6 +81,8 @@ def main():
     import paged_kv_cache_109_amd as pa
     import workloads as W
 
+    if args.workload == "chunked_prefill":
+        return bench_prefill(args)
     t0 = time.time()
     case = {"opt13b_b64": W.opt13b_b64, "large_batch_b256": W.large_batch_b256}[args.workload]()
     print(f"[bench] workload {case.name} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -201,6 +204,95 @@ def main():
                      "traffic": traffic, "alg_bytes_per_launch": alg_bytes, "avg_launch_us": part_avg_s * 1e6},
         "cpu_baseline": cpu,
     }
+    print(json.dumps(result))
+
+
+def bench_prefill(args):
+    """Chunked prefill (16 x 256-query causal chunks, bf16): a step writes the
+    chunk's K/V (reshape_and_cache, 4096 tokens) and runs the MFMA kernel."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_109_amd as pa
+    import workloads as W
+
+    case = W.chunked_prefill()
+    dev = torch.device("cuda:0")
+
+    def to_dev(a, bf=False):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.int16).view(torch.bfloat16) if bf else t).to(dev)
+
+    S, H, D, B = case.num_seqs, case.num_heads, case.head_dim, case.block_size
+    q = to_dev(case.q, True)
+    pools = [(to_dev(case.k_cache, True), to_dev(case.v_cache, True)) for _ in range(args.replicas)]
+    bt, ctx, cu = to_dev(case.block_tables), to_dev(case.context_lens), to_dev(case.cu_q_lens)
+    slots = to_dev(pa.slot_mapping(case.block_tables, case.new_seq, case.new_pos, B))
+    nk, nv = to_dev(case.new_key, True), to_dev(case.new_value, True)
+    out = torch.empty_like(q)
+    q_lens = np.diff(case.cu_q_lens)
+    max_q, max_ctx = int(q_lens.max()), case.max_context_len
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        k_cache, v_cache = pools[i % len(pools)]
+        pa.reshape_and_cache(nk, nv, k_cache, v_cache, slots)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.paged_attention_prefill_chunk(out, q, cu, k_cache, v_cache, bt, ctx, max_q, max_ctx, case.scale)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    kern_s = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+    # Causal work: query j of a sequence with c cached tokens sees c + j + 1
+    # keys; each key costs 2*D flops for q.k and 2*D for p*v.
+    c = case.context_lens - q_lens
+    keys = sum(int(q_lens[s]) * int(c[s]) + int(q_lens[s]) * (int(q_lens[s]) + 1) // 2 for s in range(S))
+    flops = 4.0 * D * H * keys
+    elt = 2
+    kv_bytes = W.logical_kv_bytes(case.context_lens, H, D, elt)
+    qo_bytes = 2 * int(q_lens.sum()) * H * D * elt
+    tflops = flops / kern_s / 1e12
+    gbps = (kv_bytes + qo_bytes) / kern_s / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        t = time.perf_counter()
+        oracle.prefill_chunk(case.q, case.cu_q_lens, case.k_cache, case.v_cache, case.block_tables,
+                             case.context_lens, case.scale, case.dtype, threads=threads)
+        dt_cpu = time.perf_counter() - t
+        cpu = {"value": int(q_lens.sum()) / dt_cpu, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"the whole chunked_prefill batch ({S} x {max_q} queries, {H} heads) once by the fp64 C "
+                         f"oracle; {dt_cpu:.2f}s"}
+    result = {
+        "metric": "chunked prefill paged attention query tokens/s (MFMA), OPT-13B shapes",
+        "value": int(q_lens.sum()) / (ms_per_step * 1e-3), "unit": "query tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": case.name, "num_seqs": S, "q_len": max_q, "num_heads": H, "head_dim": D,
+                   "block_size": B, "context_tokens": int(case.context_lens.sum()),
+                   "step": "reshape_and_cache(4096 chunk tokens) + prefill chunk kernel"},
+        "roofline": {"bound": "hbm", "kernel": "prefill_chunk_kernel", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "alg_bytes_per_launch": kv_bytes + qo_bytes, "avg_launch_us": kern_s * 1e6,
+                     "mfma_tflops": tflops, "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                     "mfma_frac": tflops / MFMA_BF16_PEAK_TFLOPS, "causal_flops_per_launch": flops},
+        "cpu_baseline": cpu,
+    }
+    print(f"[bench] prefill step {ms_per_step * 1e3:.1f} us; kernel {kern_s * 1e6:.1f} us; {tflops:.0f} TFLOP/s; "
+          f"{gbps:.0f} GB/s", file=sys.stderr, flush=True)
     print(json.dumps(result))
 
 

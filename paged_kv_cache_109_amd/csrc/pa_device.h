@@ -23,17 +23,24 @@ constexpr int kWave = 64;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// float -> bf16 bits, round to nearest even (gfx950's v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x0040u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
   _Float16 h = (_Float16)f;  // v_cvt_f16_f32: round to nearest even
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+// Two floats -> two packed 16-bit values (lo in bits 0-15), nearest even.
+template <bool kBf16>
+__device__ __forceinline__ uint32_t pack_pair(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  if constexpr (kBf16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf162_t));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2_t));
 }
 
 // ------------------------------------------------ 16-byte fragment arithmetic
@@ -95,12 +102,9 @@ __device__ __forceinline__ void frag_axpy(float *acc, float p, const uint4 &v) {
 template <Dt T>
 __device__ __forceinline__ uint4 frag_pack(const float *x) {
   uint32_t w[4];
-  if constexpr (T == Dt::F16) {
+  if constexpr (T == Dt::F16 || T == Dt::BF16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = f32_to_f16_bits(x[2 * i]) | (f32_to_f16_bits(x[2 * i + 1]) << 16);
-  } else if constexpr (T == Dt::BF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16_bits(x[2 * i]) | (f32_to_bf16_bits(x[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) w[i] = pack_pair<T == Dt::BF16>(x[2 * i], x[2 * i + 1]);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(x[i]);
