@@ -43,6 +43,7 @@ constexpr int kVRow = kPfKeys * 2 + 16;   // bytes per V^T row in LDS (padded)
 constexpr int kKBuf = kPfKeys * kKRow;    // 8704 B
 constexpr int kVBuf = kPfD * kVRow;       // 10240 B
 constexpr int kRing = 3;                  // LDS buffers (loads run two blocks ahead)
+constexpr int kTableCache = 4096;         // table entries kept in LDS (16 KB)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -73,6 +74,7 @@ template <Dt T, int B>
 __global__ __launch_bounds__(kPfWaves *kWave) void prefill_chunk_kernel(PrefillArgs a, int qtiles) {
   __shared__ __attribute__((aligned(16))) char lds_k[kRing][kKBuf];
   __shared__ __attribute__((aligned(16))) char lds_v[kRing][kVBuf];
+  __shared__ int32_t lds_table[kTableCache];
   static_assert(kPfWaves * kWave == 512, "staging maps 512 threads onto a 32-key block");
 
   const int tid = threadIdx.x;
@@ -124,10 +126,20 @@ __global__ __launch_bounds__(kPfWaves *kWave) void prefill_chunk_kernel(PrefillA
   const int64_t head_off = (int64_t)h * B * (kPfD * 2);
   const int64_t block_stride = (int64_t)a.num_heads * B * (kPfD * 2);
 
+  // The table entries of the tile's keys, copied once into LDS so the
+  // address of every K/V load is one LDS read away (longer contexts read the
+  // rest from memory).
+  const int nent = (kv_end + B - 1) / B;
+  for (int i = tid; i < min(nent, kTableCache); i += kPfWaves * kWave) {
+    const int32_t e = a.block_tables[table_row + i];
+    lds_table[i] = (e >= 0 && (int64_t)e < a.num_blocks) ? e : -1;
+  }
+  __syncthreads();
   // Physical block of logical block lb, or -1 (outside the tile's keys or the pool).
   auto entry = [&](int lb) -> int32_t {
     if (lb * B >= kv_end) return -1;
-    const int32_t e = load_uniform(a.block_tables, table_row + lb);
+    if (lb < kTableCache) return lds_table[lb];
+    const int32_t e = a.block_tables[table_row + lb];
     return (e >= 0 && (int64_t)e < a.num_blocks) ? e : -1;
   };
 
@@ -176,30 +188,51 @@ __global__ __launch_bounds__(kPfWaves *kWave) void prefill_chunk_kernel(PrefillA
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[dt][j] = 0.f;
 
+  // Lowest query position of the wave, and whether all its queries are valid:
+  // key blocks entirely at or before it need no causal mask.
+  const int wave_first = c + qbase + wave * 32;
+  const bool wave_full = __builtin_amdgcn_ballot_w64(q_ok) == ~0ull;
+
   auto compute = [&](int kb, int buf) {
-    // S^T = K Q^T over head_dim: A = K rows (permuted), B = this lane's Q.
-    f32x16 sacc;
+    // S^T = K Q^T over head_dim: A = K rows (permuted), B = this lane's Q;
+    // two independent accumulation chains (even / odd head_dim steps).
+    f32x16 s0, s1;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+    for (int j = 0; j < 16; ++j) s0[j] = s1[j] = 0.f;
     const char *krow = &lds_k[buf][k_row_perm(col) * kKRow];
 #pragma unroll
-    for (int st = 0; st < kPfD / 16; ++st) {
-      const uint4 ka = *reinterpret_cast<const uint4 *>(krow + (16 * st + 8 * half) * 2);
-      sacc = mfma<T>(ka, qf[st], sacc);
+    for (int st = 0; st < kPfD / 16; st += 2) {
+      const uint4 ka0 = *reinterpret_cast<const uint4 *>(krow + (16 * st + 8 * half) * 2);
+      const uint4 ka1 = *reinterpret_cast<const uint4 *>(krow + (16 * (st + 1) + 8 * half) * 2);
+      s0 = mfma<T>(ka0, qf[st], s0);
+      s1 = mfma<T>(ka1, qf[st + 1], s1);
     }
+    f32x16 sacc;
     // Register j holds key kb*32 + 16*(j/8) + 8*half + j%8 for this lane's query.
     float mloc = -INFINITY;
+    if (wave_full && kb * kPfKeys + kPfKeys - 1 <= wave_first) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int p = kb * kPfKeys + 16 * (j / 8) + 8 * half + (j % 8);
-      const bool ok = q_ok && p <= qpos;
-      sacc[j] = ok ? sacc[j] * a.scale_log2 : -INFINITY;
-      mloc = fmaxf(mloc, sacc[j]);
+      for (int j = 0; j < 16; ++j) {
+        sacc[j] = (s0[j] + s1[j]) * a.scale_log2;
+        mloc = fmaxf(mloc, sacc[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int p = kb * kPfKeys + 16 * (j / 8) + 8 * half + (j % 8);
+        const bool ok = q_ok && p <= qpos;
+        sacc[j] = ok ? (s0[j] + s1[j]) * a.scale_log2 : -INFINITY;
+        mloc = fmaxf(mloc, sacc[j]);
+      }
     }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-    const float m_new = fmaxf(m_run, mloc);
+    // Lazy max: the reference max moves only when a block exceeds it by more
+    // than 8 (log2 units), so weights stay <= 2^8 and O is rarely rescaled.
+    // The result is the same softmax; only the common factor differs.
+    const bool bump = mloc > m_run + 8.f;
+    const float m_new = bump ? mloc : m_run;
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    const float alpha = bump ? fast_exp2(m_run - m_use) : 1.f;
     float lsum = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -209,7 +242,7 @@ __global__ __launch_bounds__(kPfWaves *kWave) void prefill_chunk_kernel(PrefillA
     lsum += __shfl_xor(lsum, 32, kWave);
     l_run = l_run * alpha + lsum;
     m_run = m_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+    if (__builtin_amdgcn_ballot_w64(bump) != 0) {
 #pragma unroll
       for (int dt = 0; dt < kPfD / 32; ++dt)
 #pragma unroll
