@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="opt13b_b64", choices=["opt13b_b64", "large_batch_b256", "chunked_prefill"])
+    ap.add_argument("--workload", default="opt13b_b64", choices=["opt13b_b64", "large_batch_b256", "parallel_sampling", "chunked_prefill"])
     ap.add_argument("--replicas", type=int, default=2,
                     help="copies of the KV pool used in turn, so no step finds the last one's data in cache")
     ap.add_argument("--split-workers", type=int, default=0,
@@ -84,7 +84,8 @@ def main():
     if args.workload == "chunked_prefill":
         return bench_prefill(args)
     t0 = time.time()
-    case = {"opt13b_b64": W.opt13b_b64, "large_batch_b256": W.large_batch_b256}[args.workload]()
+    case = {"opt13b_b64": W.opt13b_b64, "large_batch_b256": W.large_batch_b256,
+            "parallel_sampling": W.parallel_sampling}[args.workload]()
     print(f"[bench] workload {case.name} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
@@ -100,8 +101,13 @@ def main():
     pools = [(to_dev(case.k_cache, case.dtype), to_dev(case.v_cache, case.dtype)) for _ in range(args.replicas)]
     block_tables = to_dev(case.block_tables)
     context_lens = to_dev(case.context_lens)
-    slots = to_dev(pa.slot_mapping(case.block_tables, case.new_seq, case.new_pos, B))
-    new_k, new_v = to_dev(case.new_key, case.dtype), to_dev(case.new_value, case.dtype)
+    writes = case.new_key is not None
+    if writes:
+        slots = to_dev(pa.slot_mapping(case.block_tables, case.new_seq, case.new_pos, B))
+        new_k, new_v = to_dev(case.new_key, case.dtype), to_dev(case.new_value, case.dtype)
+    copies = case.block_mapping is not None
+    if copies:
+        mapping = to_dev(case.block_mapping)
     out = torch.empty_like(q)
     max_ctx = case.max_context_len
     workers = args.split_workers
@@ -112,7 +118,7 @@ def main():
     cal_src = torch.empty(1 << 29, dtype=torch.float16, device=dev).fill_(1.0)
     cal_dst = torch.empty_like(cal_src)
     cal_dst.copy_(cal_src)
-    # Streaming-read reference on this machine: sum of a 4 GiB tensor.
+    # A torch reduction over 4 GiB, for context (not a roofline figure).
     big = torch.ones(1 << 31, dtype=torch.float16, device=dev)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -123,21 +129,30 @@ def main():
     torch.cuda.empty_cache()
 
     def step(i, ev=None):
+        # ev: four events on the launch stream -- step start, after the cache
+        # write / copy, after the partition pass, after the reduce.
         k_cache, v_cache = pools[i % len(pools)]
-        pa.reshape_and_cache(new_k, new_v, k_cache, v_cache, slots)
         if ev is not None:
             ev[0].record(stream)
+        if copies:
+            pa.copy_blocks([k_cache], [v_cache], mapping)
+        if writes:
+            pa.reshape_and_cache(new_k, new_v, k_cache, v_cache, slots)
+        if ev is not None:
+            ev[1].record(stream)
         pa.paged_attention_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, max_ctx,
                                              case.scale, workspace=ws, split_workers=workers)
         if ev is not None:
-            ev[1].record(stream)
+            ev[2].record(stream)
         pa.paged_attention_decode_reduce(out, context_lens, max_ctx, case.max_blocks_per_seq, H, D, B,
                                          workspace=ws, split_workers=workers)
+        if ev is not None:
+            ev[3].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -146,10 +161,13 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
-    part_ms = [a.elapsed_time(b) for a, b in evs]
+    part_ms = [e[1].elapsed_time(e[2]) for e in evs]
     part_avg_s = float(np.mean(part_ms)) * 1e-3
+    pre_avg_s = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    red_avg_s = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e-3
     print(f"[bench] step {ms_per_step * 1e3:.1f} us; partition pass avg {part_avg_s * 1e6:.1f} us "
-          f"(min {min(part_ms) * 1e3:.1f}, max {max(part_ms) * 1e3:.1f})", file=sys.stderr, flush=True)
+          f"(min {min(part_ms) * 1e3:.1f}, max {max(part_ms) * 1e3:.1f}); write/copy {pre_avg_s * 1e6:.1f} us; "
+          f"reduce {red_avg_s * 1e6:.1f} us", file=sys.stderr, flush=True)
 
     elt = case.elt_bytes
     kv_bytes = W.logical_kv_bytes(case.context_lens, H, D, elt)
@@ -160,6 +178,39 @@ def main():
     achieved = alg_bytes / part_avg_s / 1e9
     tokens_per_s = S / (ms_per_step * 1e-3)
     traffic = committed_traffic(case.name.rsplit("_", 1)[0])
+
+    # The other kernels of the step, each timed by its own events: algorithmic
+    # bytes are what the call must read plus what it must write.
+    components = {"decode_reduce_kernel": {"avg_us": red_avg_s * 1e6}}
+    row = H * D * elt
+    if writes:
+        T = int(case.new_key.shape[0])
+        b = 2 * (2 * T * row) + 8 * T
+        components["reshape_and_cache_kernel"] = {"tokens": T, "alg_bytes": b, "avg_us": pre_avg_s * 1e6,
+                                                  "gbps": b / pre_avg_s / 1e9}
+    if copies:
+        P = int(case.block_mapping.shape[0])
+        blk = row * B
+        b1 = 2 * (2 * P * blk) + 16 * P
+        components["copy_blocks_kernel"] = {"pairs": P, "layers": 1, "alg_bytes": b1, "avg_us": pre_avg_s * 1e6,
+                                            "gbps": b1 / pre_avg_s / 1e9}
+        # The same copy-on-write over every layer of the model in one launch.
+        L = 40
+        layers = [pools[0]] + [(pools[0][0].clone(), pools[0][1].clone()) for _ in range(L - 1)]
+        ks, vs = [k for k, _ in layers], [v for _, v in layers]
+        pa.copy_blocks(ks, vs, mapping)
+        ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a, z in ce:
+            a.record(stream)
+            pa.copy_blocks(ks, vs, mapping)
+            z.record(stream)
+        torch.cuda.synchronize()
+        t_l = float(np.mean([a.elapsed_time(z) for a, z in ce])) * 1e-3
+        components["copy_blocks_kernel_40_layers"] = {"pairs": P, "layers": L, "alg_bytes": L * b1,
+                                                      "avg_us": t_l * 1e6, "gbps": L * b1 / t_l / 1e9}
+        print(f"[bench] copy_blocks {P} pairs x {L} layers: {t_l * 1e6:.1f} us, {L * b1 / t_l / 1e9:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        del layers, ks, vs
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -195,15 +246,21 @@ def main():
         "config": {"workload": case.name, "num_seqs": S, "num_heads": H, "head_dim": D, "block_size": B,
                    "context_tokens": int(case.context_lens.sum()), "max_context_len": max_ctx,
                    "split_workers": workers or pa.decode_default_workers(tdt, D, B), "pool_replicas": args.replicas,
-                   "step": "reshape_and_cache(new tokens) + decode partitions + decode reduce"},
+                   "step": ("copy_blocks(CoW pairs) + " if copies else "")
+                   + ("reshape_and_cache(new tokens) + " if writes else "") + "decode partitions + decode reduce"},
         "effective_kv_gbps": kv_bytes / (ms_per_step * 1e-3) / 1e9,
         "pct_hbm_peak": kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "measured_stream_read_gbps": stream_read_gbps,
+        "torch_sum_read_gbps": stream_read_gbps,
         "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "alg_bytes_per_launch": alg_bytes, "avg_launch_us": part_avg_s * 1e6},
+        "components": components,
         "cpu_baseline": cpu,
     }
+    if copies:
+        shared = sorted({b for blocks in case.seq_blocks for b in blocks})
+        result["config"]["distinct_blocks_read"] = len(shared)
+        result["config"]["distinct_block_bytes"] = len(shared) * 2 * row * B
     print(json.dumps(result))
 
 
