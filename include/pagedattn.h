@@ -220,6 +220,8 @@ pa_status pa_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t n
  *                  total_q.
  *  max_q_len       host bound of the per-sequence q_len.
  *  max_context_len host bound of context_lens.
+ *  scale           multiplies q.k before the softmax; positive and finite
+ *                  (PA_ERR_INVALID_ARG otherwise).
  */
 pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32_t *cu_q_lens,
                                            const void *k_cache, const void *v_cache,

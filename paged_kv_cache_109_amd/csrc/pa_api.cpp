@@ -332,7 +332,8 @@ pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32
   if (!pa::prefill_supported(dtype, head_dim, block_size))
     return fail(PA_ERR_UNSUPPORTED, "prefill chunk is built for fp16/bf16, head_dim 128, block_size 16/32 "
                 "(got dtype %d, head_dim %d, block_size %d)", dtype, head_dim, block_size);
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
   if (num_seqs > 65535 || num_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "grid dimension exceeds 65535");
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return ok();
   if (!out || !q || !cu_q_lens || !k_cache || !v_cache || !block_tables || !context_lens)

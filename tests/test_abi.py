@@ -98,3 +98,11 @@ def test_copy_blocks_rejects_bad_arguments():
 def test_prefill_rejects_unsupported_shapes():
     f = B._lib.pa_paged_attention_prefill_chunk
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 10, 5, 100, 4, 64, 16, 64, 0.1, 0, None) == 2
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.1, float("nan"), float("inf")])
+def test_prefill_rejects_non_positive_scale(scale):
+    # bf16, head_dim 128, B=16 is a supported shape; only the scale is wrong,
+    # so the call must fail before anything is launched.
+    f = B._lib.pa_paged_attention_prefill_chunk
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 10, 5, 100, 4, 128, 16, 64, scale, 2, None) == 1

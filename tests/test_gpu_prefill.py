@@ -76,3 +76,19 @@ def test_chunked_prefill_full_size():
     c = W.chunked_prefill()
     out, ref = run_prefill(c)
     say("  max err", check_attention(out, ref, "bf16", c.name))
+
+
+def test_prefill_context_longer_than_the_lds_table():
+    """More than 4096 table entries (16,640 tokens at B=4): the kernel reads
+    the block table from memory instead of its LDS copy."""
+    c = W.make_prefill_case(2, 0, [16600, 3], 2, 128, 4, "bf16", seed=11, q_lens=[40, 7], name="long_table")
+    out, ref = run_prefill(c)
+    say("  max err", check_attention(out, ref, "bf16", c.name))
+
+
+def test_prefill_three_query_tiles():
+    """q_len 300 spans three 128-query tiles; 129 spans two with one query in
+    the second."""
+    c = W.make_prefill_case(2, 0, [1000, 0], 3, 128, 16, "f16", seed=12, q_lens=[300, 129], name="tiles")
+    out, ref = run_prefill(c)
+    say("  max err", check_attention(out, ref, "f16", c.name))
