@@ -14,23 +14,29 @@
 // (sequence, head); each wave owns 32 of them, one per MFMA column.  Two
 // workgroups share a CU, so one's barrier waits are the other's issue slots.
 // The q tiles of one (sequence, head) get workgroup ids equal mod 8, so they
-// run on one XCD and read its K/V through the same L2.  K/V stream through
-// a 3-slot LDS ring in blocks of 32 keys gathered through the block table
-// (entries cached in LDS); global loads run two blocks ahead in registers.
+// run on one XCD and read its K/V through the same L2, and the sequences are
+// taken longest first.  K/V blocks of 32 keys are gathered through the block
+// table (entries cached in LDS) straight from HBM into a 4-slot LDS ring by
+// global_load_lds_dwordx4, three blocks ahead, with no register staging; the
+// rows are stored as they are in memory, with the 16-byte chunks of each row
+// XOR-swizzled so the operand reads below do not collide in the LDS banks.
 //
 // Per block a wave computes S^T = K Q^T with 8 v_mfma_f32_32x32x16 (bf16 or
 // f16 in, fp32 out) and O^T += V^T P^T with 8 more (16 for bf16, whose P is
 // carried as a high and a low bf16 term to keep the weights' precision).
-// The loop is software-pipelined: the S^T products of block kb+1 are issued
+// V^T operands come from the row-major V with ds_read_b64_tr_b16, the LDS
+// read that transposes 16-bit elements across each group of 16 lanes.  The
+// loop is software-pipelined: the S^T products of block kb+1 are issued
 // before the softmax of block kb, so the matrix core and the vector ALU work
 // at the same time.  Working transposed keeps one query per lane column: the
 // softmax max needs one lane swap (v_permlane32_swap), the row sum stays
 // in-lane until the end, and the rescale of O is per lane.  The K rows are
 // fed to the MFMA bit-permuted (bits 2 and 3 of the key index swapped) so
 // that the accumulator registers of S^T are exactly the B operand of the
-// P V product.  V is written to LDS transposed (V^T[d][key]) so its operand
-// reads are 16 contiguous bytes.  A wave skips the key blocks past its
-// causal limit; only blocks on a wave's diagonal are masked.
+// P V product.  A wave skips the key blocks past its causal limit; only
+// blocks on a wave's diagonal are masked.
+
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -44,13 +50,26 @@ constexpr int kPfWaves = 4;              // waves per workgroup
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfQ = 32 * kPfWaves;      // queries per workgroup
 constexpr int kPfKeys = 32;              // keys per LDS block
-constexpr int kKRow = kPfD * 2 + 16;     // bytes per K row in LDS (padded)
-constexpr int kVRow = kPfKeys * 2 + 16;  // bytes per V^T row in LDS (padded)
-constexpr int kKBuf = kPfKeys * kKRow;   // 8704 B
-constexpr int kVBuf = kPfD * kVRow;      // 10240 B
-constexpr int kRing = 3;                 // LDS slots: V of kb, K of kb+1, store of kb+2
-constexpr int kTableCache = 4096;        // table entries kept in LDS (16 KB)
+constexpr int kRow = kPfD * 2;           // bytes of one K or V row
+constexpr int kSlot = kPfKeys * kRow;    // bytes of one block of K (or V) in LDS
+constexpr int kTableCache = 3072;        // table entries kept in LDS (12 KB)
 constexpr int kSortSeqs = 64;            // batches up to this size run longest first
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Position of 16-byte chunk c of LDS row r is c ^ swz(r), with swz(r) the
+// two low bits of r over the next two (a bijection of r mod 16).  LDS serves
+// 256 bytes per cycle: the 16 lanes of a K operand read hit 16 distinct rows
+// mod 16 at one chunk, so 16 distinct positions; a transposing V read covers
+// 4 aligned rows x 4 chunks per 32 lanes, and the row's low bits move the
+// chunk by whole groups of 4, so again 16 distinct positions.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// s_waitcnt immediates (vmcnt in bits 3:0, expcnt 6:4, lgkmcnt 11:8; the
+// other counters left at their maximum, i.e. not waited for).
+constexpr int kWaitVm4 = 0x0F74;
+constexpr int kWaitVm0 = 0x0F70;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -80,16 +99,25 @@ __device__ __forceinline__ float other_half(float x) {
 
 __device__ __forceinline__ uint4 load16(const char *p) { return *reinterpret_cast<const uint4 *>(p); }
 
+// A value no later code reads: the register holding it is free from here.
+__device__ __forceinline__ uint4 forget(const uint4 &v) {
+  return make_uint4(__builtin_nondeterministic_value(v.x), __builtin_nondeterministic_value(v.y),
+                    __builtin_nondeterministic_value(v.z), __builtin_nondeterministic_value(v.w));
+}
+
+
 }  // namespace
 
 // kLong: contexts longer than kTableCache*B tokens read their table entries
 // from global memory instead of the LDS copy.
 template <Dt T, int B, bool kLong>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_chunk_kernel(PrefillArgs a, int qtiles) {
-  __shared__ __attribute__((aligned(16))) char lds_k[kRing][kKBuf];
-  __shared__ __attribute__((aligned(16))) char lds_v[kRing][kVBuf];
+  // The LDS ring: one array per slot, so the compiler can tell the slot a
+  // read uses from the slots the in-flight loads write.
+  __shared__ __attribute__((aligned(1024))) char k_0[kSlot], k_1[kSlot], k_2[kSlot], k_3[kSlot];
+  __shared__ __attribute__((aligned(1024))) char v_0[kSlot], v_1[kSlot], v_2[kSlot], v_3[kSlot];
   __shared__ int32_t lds_table[kLong ? 1 : kTableCache];
-  static_assert(kPfThreads == 256, "staging maps 256 threads onto a 32-key block");
+  static_assert(kPfThreads == 256, "loads map 256 threads onto a 32-key block");
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -175,21 +203,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_chunk_kernel(PrefillArg
     __syncthreads();
   }
 
-  // Staging of one 32-key block: per thread two 16-byte K chunks and two V
-  // chunks.  K: keys r0 = tid/16 and r0 + 16 of the block, columns
-  // 8*(tid%16) .. +8.  V: key tid%32, columns 8*(tid/32) and 64 + 8*(tid/32)
-  // (consecutive lanes, consecutive keys, so the transposed LDS writes do not
-  // collide).  The in-block part of each address is fixed per lane; only the
-  // table entry changes with the block.  Every call issues all four loads
-  // (keys past the table end read the last entry's block), and V rows of
-  // keys at or past kv_end are zeroed when stored -- their K rows need no
-  // zeroing, because those keys are masked out of every query's softmax.
-  const int r0 = tid / 16, rv = tid % 32;
-  const uint32_t lane_k0 = (uint32_t)((r0 & (B - 1)) * (kPfD * 2) + (tid % 16) * 16);
-  const uint32_t lane_k1 = (uint32_t)(((r0 + 16) & (B - 1)) * (kPfD * 2) + (tid % 16) * 16);
-  const uint32_t lane_v = (uint32_t)((rv & (B - 1)) * (kPfD * 2) + (tid / 32) * 16);
   auto entry = [&](int lb) __attribute__((always_inline)) -> uint32_t {
-    lb = min(lb, nent - 1);
     if constexpr (kLong) {
       const int32_t e = a.block_tables[table_row + lb];
       return (e >= 0 && (int64_t)e < a.num_blocks) ? (uint32_t)e : 0u;
@@ -197,37 +211,56 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_chunk_kernel(PrefillArg
       return (uint32_t)lds_table[lb];
     }
   };
-  struct Stage {
-    uint4 k0, k1, v[2];
-    bool vok;
+  auto kslot = [&](auto sc) __attribute__((always_inline)) -> char * {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return k_0;
+    else if constexpr (S == 1) return k_1;
+    else if constexpr (S == 2) return k_2;
+    else return k_3;
   };
-  auto load_block = [&](int kb, Stage &st) __attribute__((always_inline)) {
-    const int lb = kb * (kPfKeys / B);
-    const char *k0 = kbase + ((uint64_t)entry(lb + r0 / B) * block_stride + lane_k0);
-    const char *k1 = kbase + ((uint64_t)entry(lb + (r0 + 16) / B) * block_stride + lane_k1);
-    const char *v = vbase + ((uint64_t)entry(lb + rv / B) * block_stride + lane_v);
-    st.vok = kb * kPfKeys + rv < kv_end;
-    st.k0 = load16(k0);
-    st.k1 = load16(k1);
-    st.v[0] = load16(v);
-    st.v[1] = load16(v + 128);
+  auto vslot = [&](auto sc) __attribute__((always_inline)) -> char * {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return v_0;
+    else if constexpr (S == 1) return v_1;
+    else if constexpr (S == 2) return v_2;
+    else return v_3;
   };
-  auto store_block = [&](int buf, const Stage &st) __attribute__((always_inline)) {
-    char *kd = &lds_k[buf][r0 * kKRow + (tid % 16) * 16];
-    *reinterpret_cast<uint4 *>(kd) = st.k0;
-    *reinterpret_cast<uint4 *>(kd + 16 * kKRow) = st.k1;
-    // Masks applied per word (a select between whole vectors would be turned
-    // into a select between their addresses, forcing them into memory).
-    const uint32_t mv = st.vok ? ~0u : 0u;
-    const int dc = 8 * (tid / 32);
-#pragma unroll
-    for (int part = 0; part < 2; ++part) {
-      const uint32_t w4[4] = {st.v[part].x & mv, st.v[part].y & mv, st.v[part].z & mv, st.v[part].w & mv};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint16_t *>(&lds_v[buf][(dc + 64 * part + e) * kVRow + rv * 2]) =
-            (uint16_t)(w4[e / 2] >> (16 * (e % 2)));
-    }
+
+  // Loading one 32-key block: each wave moves 4 rows of K and 4 of V per
+  // instruction (64 lanes x 16 bytes land contiguously in LDS), rows
+  // 4*wave .. +3 and 16 + 4*wave .. +3.  Lane l fills position l%16 of its
+  // row with chunk (l%16) ^ swz(row) of the K/V row.  Keys at or past kv_end
+  // read the row of key kv_end-1 instead: their scores are masked and their
+  // weights are 0, and a real (finite) V row keeps 0 * V finite.
+  const int r0 = 4 * wave + lane / 16;  // swz(r0 + 16) == swz(r0)
+  const uint32_t chunk_off = (uint32_t)(16 * ((lane % 16) ^ swz(r0)));
+  // A block's load in two steps, so the table lookup can run well ahead of
+  // the loads: the two table entries of this thread's rows, then the four
+  // loads into ring slot `sc`.
+  struct Rows {
+    uint32_t e0, e1;
+    int key0, key1;
+  };
+  auto rows = [&](int kb) __attribute__((always_inline)) -> Rows {
+    Rows r;
+    r.key0 = min(kb * kPfKeys + r0, kv_end - 1);
+    r.key1 = min(kb * kPfKeys + r0 + 16, kv_end - 1);
+    r.e0 = entry(r.key0 / B);
+    r.e1 = entry(r.key1 / B);
+    return r;
+  };
+  auto issue_half = [&](const Rows &r, int part, auto sc) __attribute__((always_inline)) {
+    const uint32_t e = part ? r.e1 : r.e0;
+    const int key = part ? r.key1 : r.key0;
+    const uint64_t off = (uint64_t)e * block_stride + (uint32_t)((key & (B - 1)) * kRow) + chunk_off;
+    const int dst = 1024 * (wave + 4 * part);
+    __builtin_amdgcn_global_load_lds(kbase + off, (lds_char *)(kslot(sc) + dst), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vbase + off, (lds_char *)(vslot(sc) + dst), 16, 0, 0);
+  };
+  auto load_block = [&](int kb, auto sc) __attribute__((always_inline)) {
+    const Rows r = rows(kb);
+    issue_half(r, 0, sc);
+    issue_half(r, 1, sc);
   };
 
   // ---- running softmax state of this lane's query, and O^T accumulators.
@@ -246,126 +279,231 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_chunk_kernel(PrefillArg
   const bool wave_full = __builtin_amdgcn_ballot_w64(q_ok) == ~0ull;
   const float sc = a.scale_log2;  // > 0 (checked by the host)
 
-  // S^T of the block in LDS slot `slot` for this lane's query: register j
-  // holds the raw q.k of key 16*(j/8) + 8*half + j%8 of the block.
-  auto qk = [&](int slot) __attribute__((always_inline)) -> f32x16 {
+  // Per-lane LDS offsets of the MFMA operands.  K: row R = k_row_perm(col),
+  // chunk 2*st + half, at its swizzled position.  V^T (transposing reads):
+  // for rows d = 32*dt + col and keys 16*t + 8*half + 4*i .. +3, lane j of
+  // each 16-lane group points at 4 elements of key 16*t + 8*half + 4*i +
+  // j/4, columns 32*dt + 16*(lane/16 % 2) + 4*(j%4) .. +3; the read hands
+  // lane j element e of the lane 4*e + j/4 that pointed there.  The offset
+  // of read (dt, i) is fixed per lane; t adds 16 rows.
+  uint32_t k_off[kPfD / 16];
+  {
+    const int R = k_row_perm(col);
+#pragma unroll
+    for (int st = 0; st < kPfD / 16; ++st) k_off[st] = (uint32_t)(R * kRow + 16 * ((2 * st + half) ^ swz(R)));
+  }
+  uint32_t v_off[kPfD / 32][2];
+  {
+    const int j = lane % 16, gm = (lane / 16) % 2;
+#pragma unroll
+    for (int dt = 0; dt < kPfD / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int key = 8 * half + 4 * i + j / 4;
+        const int chunk = 4 * dt + 2 * gm + (j % 4) / 2;
+        v_off[dt][i] = (uint32_t)(key * kRow + 16 * (chunk ^ swz(key)) + 8 * (j % 2));
+      }
+  }
+
+  // ---- operand reads and products.
+  // K operand st of the block in slot `sc` (A of S^T = K Q^T).
+  auto kread = [&](auto sc, int st) __attribute__((always_inline)) -> uint4 {
+    return load16(kslot(sc) + k_off[st]);
+  };
+  // V^T operand (t, dt) of the block in slot `sc` (A of O^T += V^T P^T).
+  auto vread = [&](auto sc, int t, int dt) __attribute__((always_inline)) -> uint4 {
+    const lds_char *vb_ = (const lds_char *)vslot(sc);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (v4i16 __attribute__((address_space(3))) *)(vb_ + v_off[dt][0] + 16 * kRow * t));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (v4i16 __attribute__((address_space(3))) *)(vb_ + v_off[dt][1] + 16 * kRow * t));
+    return make_uint4(__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                      __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                      __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                      __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3)));
+  };
+  // S^T of the block in slot `sc` in one go (used before the loop).
+  auto qk = [&](auto sc) __attribute__((always_inline)) -> f32x16 {
     f32x16 sacc;
 #pragma unroll
     for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
-    const char *krow = &lds_k[slot][k_row_perm(col) * kKRow];
 #pragma unroll
-    for (int st = 0; st < kPfD / 16; ++st)
-      sacc = mfma<T>(load16(krow + (16 * st + 8 * half) * 2), qf[st], sacc);
+    for (int st = 0; st < kPfD / 16; ++st) sacc = mfma<T>(kread(sc, st), qf[st], sacc);
     return sacc;
   };
 
-  // One block of a wave: the softmax of block kb (raw scores `scur`) into
-  // P^T, O^T += V^T P^T, and -- issued among the softmax instructions so the
-  // matrix core is busy meanwhile -- S^T of block kb+1 into `snext`.
-  auto compute = [&](int kb, f32x16 &scur, f32x16 &snext) __attribute__((always_inline)) {
+  // PV MFMA n of a block: t = n / (kPV/2), then the four accumulators in
+  // turn (P_hi first, then P_lo for bf16), so consecutive MFMAs never depend
+  // on each other.
+  constexpr int kPV = (T == Dt::BF16) ? 16 : 8;
+  auto pv = [&](int n, const uint4 (&va)[2][kPfD / 32], const uint4 (&pb)[2], const uint4 (&pl)[2])
+                __attribute__((always_inline)) {
+    const int t = n / (kPV / 2), r = n % (kPV / 2), dt = r % 4;
+    o[dt] = mfma<T>(va[t][dt], r < 4 ? pb[t] : pl[t], o[dt]);
+  };
+
+  // The weights of one block from its masked scores x against reference m:
+  // p = 2^(x*scale_log2 - m), their sum, and P^T packed as the B operand (k
+  // step t holds keys 16t + 8*half .. +8 = registers 8t .. 8t+7).  bf16
+  // keeps only 8 significant bits, too few for the weights, so P is carried
+  // as P_hi + P_lo (P_hi the top 16 bits of the float, P_lo the rest rounded
+  // to bf16: about 16 bits together) and the product is formed twice; fp16's
+  // 11 bits are enough on their own.  `pair` q covers registers 2q, 2q+1.
+  auto weigh_pair = [&](const f32x16 &x, float m, int q, float &lsum, uint4 (&pb)[2], uint4 (&pl)[2])
+                        __attribute__((always_inline)) {
+    const float p0 = fast_exp2(fmaf(x[2 * q], sc, -m));
+    const float p1 = fast_exp2(fmaf(x[2 * q + 1], sc, -m));
+    lsum += p0;
+    lsum += p1;
+    uint32_t hw, lw = 0;
+    if constexpr (T == Dt::BF16) {
+      const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+      hw = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // high halves: p1 | p0
+      lw = pack_pair<true>(p0 - __uint_as_float(b0 & 0xffff0000u), p1 - __uint_as_float(b1 & 0xffff0000u));
+    } else {
+      hw = pack_pair<false>(p0, p1);
+    }
+    const int t = q / 4, e = q % 4;
+    if (e == 0) { pb[t].x = hw; pl[t].x = lw; }
+    else if (e == 1) { pb[t].y = hw; pl[t].y = lw; }
+    else if (e == 2) { pb[t].z = hw; pl[t].z = lw; }
+    else { pb[t].w = hw; pl[t].w = lw; }
+  };
+
+  // One half-step of a wave that still has block h to do (raw S^T of block
+  // h in `scur`).  Two fenced regions fix the issue order so each MFMA has
+  // vector or memory work issued under it:
+  //  A: the 8 MFMAs of S^T of block h+1 (K from slot KS, into `snext`), with
+  //     the softmax of block h, the reads of block h's V^T operands (slot
+  //     VS) and of block h+3's table entries between them;
+  //  B: the P V products of block h, with block h+3's loads (into slot DS).
+  // Between them sits the lazy-max check, which rarely fires.
+  auto compute = [&](int h, f32x16 &scur, f32x16 &snext, auto vs, auto ks, auto ds)
+                     __attribute__((always_inline)) {
     f32x16 &x = scur;
-    if (!(wave_full && kb * kPfKeys + kPfKeys - 1 <= wave_first)) {
-      // Register j is key kb*32 + 8*half + (16*(j/8) + j%8); it is visible
+    if (!(wave_full && h * kPfKeys + kPfKeys - 1 <= wave_first)) {
+      // Register j is key h*32 + 8*half + (16*(j/8) + j%8); it is visible
       // to this lane's query iff that is <= qpos.
-      const int lim = q_ok ? qpos - kb * kPfKeys - 8 * half : -1;
+      const int lim = q_ok ? qpos - h * kPfKeys - 8 * half : -1;
 #pragma unroll
       for (int j = 0; j < 16; ++j) x[j] = (16 * (j / 8) + j % 8 <= lim) ? x[j] : -INFINITY;
     }
-    snext = qk((kb + 1) % kRing);
-    float mx = fmaxf(x[0], x[1]);
+    const float m0 = (m_run == -INFINITY) ? 0.f : m_run;
+    float lsum = 0.f, mx = -INFINITY;
+    uint4 ka[kPfD / 16], va[2][kPfD / 32], pb[2], pl[2];
+    const Rows nr = rows(h + 3);
+    ka[0] = kread(ks, 0);
+    ka[1] = kread(ks, 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 2; j < 16; ++j) mx = fmaxf(mx, x[j]);
-    mx = fmaxf(mx, other_half(mx));
-    // Lazy max: the reference max moves only when a block exceeds it by more
-    // than 8 (log2 units), so weights stay <= 2^8 and O is rarely rescaled.
-    // The result is the same softmax; only the common factor differs.
-    const float mblk = mx * sc;
-    const bool bump = mblk > m_run + 8.f;
-    const float m_new = bump ? mblk : m_run;
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = bump ? fast_exp2(m_run - m_use) : 1.f;
-    float p[16];
-    float lsum = 0.f;
+    for (int i = 0; i < kPfD / 16; ++i) {
+      snext = mfma<T>(ka[i], qf[i], i == 0 ? f32x16{} : snext);
+      if (i + 2 < kPfD / 16) ka[i + 2] = kread(ks, i + 2);
+      va[i / 4][i % 4] = vread(vs, i / 4, i % 4);
+      if (i == 0) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      p[j] = fast_exp2(fmaf(x[j], sc, -m_use));
-      lsum += p[j];
-    }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-    // P^T as the B operand: k step t holds keys 16t + 8*half .. +8 =
-    // registers 8t .. 8t+7.  bf16 keeps only 8 significant bits, too few for
-    // the weights, so P is carried as P_hi + P_lo (P_hi the top 16 bits of
-    // the float, P_lo the rest rounded to bf16: about 16 bits together) and
-    // the product is formed twice; fp16's 11 bits are enough on their own.
-    uint4 pb[2], pl[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = p[8 * t + 2 * e], p1 = p[8 * t + 2 * e + 1];
-        if constexpr (T == Dt::BF16) {
-          const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
-          hw[e] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // high halves: p1 | p0
-          lw[e] = pack_pair<true>(p0 - __uint_as_float(b0 & 0xffff0000u), p1 - __uint_as_float(b1 & 0xffff0000u));
-        } else {
-          hw[e] = pack_pair<false>(p0, p1);
-          lw[e] = 0;
-        }
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, x[j]);
+      } else {
+        weigh_pair(x, m0, i - 1, lsum, pb, pl);
+        if (i == 1) weigh_pair(x, m0, 7, lsum, pb, pl);
       }
-      pb[t] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      pl[t] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+    // The speculative weights stay here, ahead of the check (the compiler
+    // would otherwise move them into the branch that keeps them).
+    asm volatile("" ::"v"(pb[0].x), "v"(pb[0].y), "v"(pb[0].z), "v"(pb[0].w), "v"(pb[1].x), "v"(pb[1].y),
+                 "v"(pb[1].z), "v"(pb[1].w), "v"(pl[0].x), "v"(pl[0].y), "v"(pl[0].z), "v"(pl[0].w), "v"(pl[1].x),
+                 "v"(pl[1].y), "v"(pl[1].z), "v"(pl[1].w), "v"(lsum));
+    // Lazy max: the reference max m_run moves only when a block exceeds it
+    // by more than 8 (log2 units), so weights stay <= 2^8 and O is rarely
+    // rescaled; the result is the same softmax, only the common factor
+    // differs.  The weights above were formed against m_run (each half of
+    // the wave judging its own 16 keys of the query); if the block moves the
+    // max of any query, the halves agree on it, O is rescaled and the
+    // weights are formed again.
+    if (__builtin_amdgcn_ballot_w64(mx * sc > m_run + 8.f) != 0) {
+      mx = fmaxf(mx, other_half(mx));
+      const float mblk = mx * sc;
+      const bool bump = mblk > m_run + 8.f;
+      const float m_new = bump ? mblk : m_run;
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = bump ? fast_exp2(m_run - m_use) : 1.f;
+      l_run *= alpha;
+      m_run = m_new;
 #pragma unroll
       for (int dt = 0; dt < kPfD / 32; ++dt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
+      lsum = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) weigh_pair(x, m_use, q, lsum, pb, pl);
     }
-    // O^T += V^T P^T: A = V^T rows (d = 32*dt + col), 8 keys at 16t + 8*half.
+    l_run += lsum;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int dt = 0; dt < kPfD / 32; ++dt) {
-      const char *vrow = &lds_v[kb % kRing][(32 * dt + col) * kVRow];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint4 va = load16(vrow + (16 * t + 8 * half) * 2);
-        o[dt] = mfma<T>(va, pb[t], o[dt]);
-        if constexpr (T == Dt::BF16) o[dt] = mfma<T>(va, pl[t], o[dt]);
-      }
+    for (int n = 0; n < kPV; ++n) {
+      pv(n, va, pb, pl);
+      if (n == 0) issue_half(nr, 0, ds);
+      if (n == 2) issue_half(nr, 1, ds);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
+  auto step = [&](int h, f32x16 &scur, f32x16 &snext, auto vs, auto ks, auto ds) __attribute__((always_inline)) {
+    if (h < wave_nkb) compute(h, scur, snext, vs, ks, ds);
+    else load_block(h + 3, ds);
+  };
 
-  // Pipeline.  At the top of a half-step for block kb: blocks kb and kb+1
-  // are in LDS (slots kb%3, (kb+1)%3), one staging set holds block kb+2
-  // (loaded during the previous half-step), and the wave holds S^T of block
-  // kb.  The half-step loads block kb+3 into the other set, computes block kb
-  // (and S^T of kb+1), stores kb+2 into the slot block kb-1 used, and ends at
-  // a barrier.  The loop runs whole pairs of half-steps (an odd block count
-  // ends with an idle half-step), so the two staging sets and the two score
-  // tiles keep fixed registers.
-  Stage sx, sy;
+  // Wait until at most `kWait` of this wave's loads are in flight, then
+  // meet the other waves.  The loads write LDS directly, so a barrier with
+  // the usual memory fence would wait for all of them; this one waits only
+  // for the older blocks (the empty asm statements keep the compiler from
+  // moving LDS accesses across it).
+  auto sync_blocks = [&](auto wait) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(decltype(wait)::value);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Pipeline.  Half-step h starts with blocks h and h+1 in the ring (slots
+  // h%4, (h+1)%4) and block h+2's loads in flight; it issues block h+3's
+  // loads into the slot block h-1 used, computes, waits for block h+2 and
+  // ends at a barrier.  Loads are issued at every half-step, also past the
+  // last block (their addresses stay inside the caches), so each wait covers
+  // the same number of younger loads.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  using Wait4 = std::integral_constant<int, kWaitVm4>;
   f32x16 sa, sb;
 #pragma unroll
   for (int j = 0; j < 16; ++j) sa[j] = sb[j] = 0.f;
   if (nkb > 0) {
-    load_block(0, sx);
-    load_block(1, sy);
-    store_block(0, sx);
-    store_block(1, sy);
-    load_block(2, sx);
-  }
-  __syncthreads();
-  if (0 < wave_nkb) sa = qk(0);
-  for (int kb = 0; kb < nkb; kb += 2) {
-    load_block(kb + 3, sy);
-    if (kb < wave_nkb) compute(kb, sa, sb);
-    if (kb + 2 < nkb) store_block((kb + 2) % kRing, sx);
-    __syncthreads();
-    load_block(kb + 4, sx);
-    if (kb + 1 < wave_nkb) compute(kb + 1, sb, sa);
-    if (kb + 3 < nkb) store_block((kb + 3) % kRing, sy);
-    __syncthreads();
+    // The Q fragments are in registers before any block load is issued (so
+    // no later wait for them has to count the block loads).
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    load_block(0, S0{});
+    load_block(1, S1{});
+    load_block(2, S2{});
+    sync_blocks(Wait4{});  // blocks 0 and 1 are in
+    if (0 < wave_nkb) sa = qk(S0{});
+    for (int h = 0;; h += 4) {
+      step(h, sa, sb, S0{}, S1{}, S3{});
+      sync_blocks(Wait4{});
+      if (h + 1 >= nkb) break;
+      step(h + 1, sb, sa, S1{}, S2{}, S0{});
+      sync_blocks(Wait4{});
+      if (h + 2 >= nkb) break;
+      step(h + 2, sa, sb, S2{}, S3{}, S1{});
+      sync_blocks(Wait4{});
+      if (h + 3 >= nkb) break;
+      step(h + 3, sb, sa, S3{}, S0{}, S2{});
+      sync_blocks(Wait4{});
+      if (h + 4 >= nkb) break;
+    }
+    // No load may still be writing this workgroup's LDS when it exits.
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
   }
 
   // ---- write this lane's query: O^T register j of tile dt is d = 32*dt + 8*(j/4) + 4*half + j%4.
