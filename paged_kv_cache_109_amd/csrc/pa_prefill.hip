@@ -443,14 +443,14 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_chunk_kernel(PrefillArg
 #pragma unroll
     for (int n = 0; n < kPV; ++n) {
       pv(n, va, pb, pl);
-      if (n == 0) issue_half(nr, 0, ds);
-      if (n == 2) issue_half(nr, 1, ds);
+      if (n == 0 && h + 3 < nkb) issue_half(nr, 0, ds);
+      if (n == 2 && h + 3 < nkb) issue_half(nr, 1, ds);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto step = [&](int h, f32x16 &scur, f32x16 &snext, auto vs, auto ks, auto ds) __attribute__((always_inline)) {
     if (h < wave_nkb) compute(h, scur, snext, vs, ks, ds);
-    else load_block(h + 3, ds);
+    else if (h + 3 < nkb) load_block(h + 3, ds);
   };
 
   // Wait until at most `kWait` of this wave's loads are in flight, then
@@ -468,14 +468,19 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_chunk_kernel(PrefillArg
   // Pipeline.  Half-step h starts with blocks h and h+1 in the ring (slots
   // h%4, (h+1)%4) and block h+2's loads in flight; it issues block h+3's
   // loads into the slot block h-1 used, computes, waits for block h+2 and
-  // ends at a barrier.  Loads are issued at every half-step, also past the
-  // last block (their addresses stay inside the caches), so each wait covers
-  // the same number of younger loads.
+  // ends at a barrier.
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
   using S3 = std::integral_constant<int, 3>;
   using Wait4 = std::integral_constant<int, kWaitVm4>;
+  using Wait0 = std::integral_constant<int, kWaitVm0>;
+  // End of half-step h: while blocks are still being loaded, the four loads
+  // of block h+3 may stay in flight; past the last block none were issued.
+  auto end_step = [&](int h) __attribute__((always_inline)) {
+    if (h + 3 < nkb) sync_blocks(Wait4{});
+    else sync_blocks(Wait0{});
+  };
   f32x16 sa, sb;
 #pragma unroll
   for (int j = 0; j < 16; ++j) sa[j] = sb[j] = 0.f;
@@ -484,26 +489,28 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_chunk_kernel(PrefillArg
     // no later wait for them has to count the block loads).
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     load_block(0, S0{});
-    load_block(1, S1{});
-    load_block(2, S2{});
-    sync_blocks(Wait4{});  // blocks 0 and 1 are in
+    if (nkb > 1) load_block(1, S1{});
+    if (nkb > 2) {
+      load_block(2, S2{});
+      sync_blocks(Wait4{});  // blocks 0 and 1 are in
+    } else {
+      sync_blocks(Wait0{});
+    }
     if (0 < wave_nkb) sa = qk(S0{});
     for (int h = 0;; h += 4) {
       step(h, sa, sb, S0{}, S1{}, S3{});
-      sync_blocks(Wait4{});
+      end_step(h);
       if (h + 1 >= nkb) break;
       step(h + 1, sb, sa, S1{}, S2{}, S0{});
-      sync_blocks(Wait4{});
+      end_step(h + 1);
       if (h + 2 >= nkb) break;
       step(h + 2, sa, sb, S2{}, S3{}, S1{});
-      sync_blocks(Wait4{});
+      end_step(h + 2);
       if (h + 3 >= nkb) break;
       step(h + 3, sb, sa, S3{}, S0{}, S2{});
-      sync_blocks(Wait4{});
+      end_step(h + 3);
       if (h + 4 >= nkb) break;
     }
-    // No load may still be writing this workgroup's LDS when it exits.
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
   }
 
   // ---- write this lane's query: O^T register j of tile dt is d = 32*dt + 8*(j/4) + 4*half + j%4.
