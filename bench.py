@@ -49,23 +49,35 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_digest() -> str:
-    src = open(os.path.join(ROOT, "paged_kv_cache_109_amd", "csrc", "pa_decode.hip"), "rb").read()
+def kernel_source_digest(source: str = "pa_decode.hip") -> str:
+    src = open(os.path.join(ROOT, "paged_kv_cache_109_amd", "csrc", source), "rb").read()
     return hashlib.sha256(src).hexdigest()[:16]
 
 
-def committed_traffic(workload: str):
-    """HBM bytes per partition-kernel launch from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"decode_partition_{workload}_counters.md")
+def committed_traffic(profile: str, source: str = "pa_decode.hip"):
+    """HBM bytes per launch of a kernel from its committed rocprofv3 counter
+    summary (profiles/<profile>_counters.md), if that summary was taken on
+    the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{profile}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != kernel_source_digest():
+    if not m or not t or m.group(1) != kernel_source_digest(source):
         return None
     return float(t.group(1))
+
+
+def calibrate_counters(torch, dev):
+    """A plain 1 GiB device copy, the reference the HBM byte counters are
+    scaled by (its FETCH_SIZE and WRITE_SIZE must read 1 GiB each)."""
+    src = torch.empty(1 << 29, dtype=torch.float16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def main():
@@ -114,10 +126,7 @@ def main():
     ws = pa.alloc_decode_workspace(S, H, D, max_ctx, B, workers, device=dev)
     stream = torch.cuda.current_stream()
 
-    # Calibration kernel for the HBM byte counters: a plain 1 GiB copy.
-    cal_src = torch.empty(1 << 29, dtype=torch.float16, device=dev).fill_(1.0)
-    cal_dst = torch.empty_like(cal_src)
-    cal_dst.copy_(cal_src)
+    calibrate_counters(torch, dev)
     # A torch reduction over 4 GiB, for context (not a roofline figure).
     big = torch.ones(1 << 31, dtype=torch.float16, device=dev)
     torch.cuda.synchronize()
@@ -125,7 +134,7 @@ def main():
     big.sum()
     e0.record(); big.sum(); e1.record(); torch.cuda.synchronize()
     stream_read_gbps = big.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del big, cal_src, cal_dst
+    del big
     torch.cuda.empty_cache()
 
     def step(i, ev=None):
@@ -177,7 +186,7 @@ def main():
     alg_bytes = kv_bytes + 2 * S * H * D * elt + 4 * nblocks + 4 * S
     achieved = alg_bytes / part_avg_s / 1e9
     tokens_per_s = S / (ms_per_step * 1e-3)
-    traffic = committed_traffic(case.name.rsplit("_", 1)[0])
+    traffic = committed_traffic("decode_partition_" + case.name.rsplit("_", 1)[0])
 
     # The other kernels of the step, each timed by its own events: algorithmic
     # bytes are what the call must read plus what it must write.
@@ -290,6 +299,7 @@ def bench_prefill(args):
     q_lens = np.diff(case.cu_q_lens)
     max_q, max_ctx = int(q_lens.max()), case.max_context_len
     stream = torch.cuda.current_stream()
+    calibrate_counters(torch, dev)
 
     def step(i, ev=None):
         k_cache, v_cache = pools[i % len(pools)]
@@ -342,7 +352,8 @@ def bench_prefill(args):
                    "block_size": B, "context_tokens": int(case.context_lens.sum()),
                    "step": "reshape_and_cache(4096 chunk tokens) + prefill chunk kernel"},
         "roofline": {"bound": "hbm", "kernel": "prefill_chunk_kernel", "achieved": gbps, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                     "traffic": committed_traffic("prefill_chunk_chunked_prefill", "pa_prefill.hip"),
                      "alg_bytes_per_launch": kv_bytes + qo_bytes, "avg_launch_us": kern_s * 1e6,
                      "mfma_tflops": tflops, "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                      "mfma_frac": tflops / MFMA_BF16_PEAK_TFLOPS, "causal_flops_per_launch": flops},
