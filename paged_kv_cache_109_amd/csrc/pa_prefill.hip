@@ -342,42 +342,29 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_chunk_kernel(PrefillArg
     o[dt] = mfma<T>(va[t][dt], r < 4 ? pb[t] : pl[t], o[dt]);
   };
 
-  // The weights of one block from its masked scores x against reference m:
+  // Weights of one block from its masked scores x against the reference m:
   // p = 2^(x*scale_log2 - m), their sum, and P^T packed as the B operand (k
   // step t holds keys 16t + 8*half .. +8 = registers 8t .. 8t+7).  bf16
   // keeps only 8 significant bits, too few for the weights, so P is carried
   // as P_hi + P_lo (P_hi the top 16 bits of the float, P_lo the rest rounded
   // to bf16: about 16 bits together) and the product is formed twice; fp16's
-  // 11 bits are enough on their own.  `pair` q covers registers 2q, 2q+1.
-  auto weigh_pair = [&](const f32x16 &x, float m, int q, float &lsum, uint4 (&pb)[2], uint4 (&pl)[2])
-                        __attribute__((always_inline)) {
-    const float p0 = fast_exp2(fmaf(x[2 * q], sc, -m));
-    const float p1 = fast_exp2(fmaf(x[2 * q + 1], sc, -m));
-    lsum += p0;
-    lsum += p1;
-    uint32_t hw, lw = 0;
-    if constexpr (T == Dt::BF16) {
-      const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
-      hw = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // high halves: p1 | p0
-      lw = pack_pair<true>(p0 - __uint_as_float(b0 & 0xffff0000u), p1 - __uint_as_float(b1 & 0xffff0000u));
-    } else {
-      hw = pack_pair<false>(p0, p1);
-    }
-    const int t = q / 4, e = q % 4;
-    if (e == 0) { pb[t].x = hw; pl[t].x = lw; }
-    else if (e == 1) { pb[t].y = hw; pl[t].y = lw; }
-    else if (e == 2) { pb[t].z = hw; pl[t].z = lw; }
-    else { pb[t].w = hw; pl[t].w = lw; }
-  };
+  // 11 bits are enough on their own.
 
   // One half-step of a wave that still has block h to do (raw S^T of block
-  // h in `scur`).  Two fenced regions fix the issue order so each MFMA has
-  // vector or memory work issued under it:
-  //  A: the 8 MFMAs of S^T of block h+1 (K from slot KS, into `snext`), with
-  //     the softmax of block h, the reads of block h's V^T operands (slot
-  //     VS) and of block h+3's table entries between them;
-  //  B: the P V products of block h, with block h+3's loads (into slot DS).
-  // Between them sits the lazy-max check, which rarely fires.
+  // h in `scur`).  First the lazy-max check: the reference max m_run moves
+  // only when a block exceeds it by more than 8 (log2 units), so weights
+  // stay <= 2^8 and O is rarely rescaled; the result is the same softmax,
+  // only the common factor differs.  Each half of the wave judges its own 16
+  // keys of the query, and only if some query's max moves do the halves
+  // agree on it and rescale O (which holds blocks up to h-1).  Then one
+  // fenced region of 8 + kPV MFMA slots fixes the issue order so the
+  // matrix core and the vector ALU work at once:
+  //  - slots 0..7: S^T of block h+1 (K from slot KS, into `snext`), with the
+  //    weights of keys 0..15 of block h and the reads of block h's V^T
+  //    operands (slot VS) under them;
+  //  - the first half of the P V products (keys 0..15), with the weights of
+  //    keys 16..31 under them;
+  //  - the second half, with block h+3's loads (into slot DS) under them.
   auto compute = [&](int h, f32x16 &scur, f32x16 &snext, auto vs, auto ks, auto ds)
                      __attribute__((always_inline)) {
     f32x16 &x = scur;
@@ -388,65 +375,76 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_chunk_kernel(PrefillArg
 #pragma unroll
       for (int j = 0; j < 16; ++j) x[j] = (16 * (j / 8) + j % 8 <= lim) ? x[j] : -INFINITY;
     }
-    const float m0 = (m_run == -INFINITY) ? 0.f : m_run;
-    float lsum = 0.f, mx = -INFINITY;
-    uint4 ka[kPfD / 16], va[2][kPfD / 32], pb[2], pl[2];
-    const Rows nr = rows(h + 3);
-    ka[0] = kread(ks, 0);
-    ka[1] = kread(ks, 1);
-    __builtin_amdgcn_sched_barrier(0);
+    float mx = fmaxf(x[0], x[1]);
 #pragma unroll
-    for (int i = 0; i < kPfD / 16; ++i) {
-      snext = mfma<T>(ka[i], qf[i], i == 0 ? f32x16{} : snext);
-      if (i + 2 < kPfD / 16) ka[i + 2] = kread(ks, i + 2);
-      va[i / 4][i % 4] = vread(vs, i / 4, i % 4);
-      if (i == 0) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, x[j]);
-      } else {
-        weigh_pair(x, m0, i - 1, lsum, pb, pl);
-        if (i == 1) weigh_pair(x, m0, 7, lsum, pb, pl);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // The speculative weights stay here, ahead of the check (the compiler
-    // would otherwise move them into the branch that keeps them).
-    asm volatile("" ::"v"(pb[0].x), "v"(pb[0].y), "v"(pb[0].z), "v"(pb[0].w), "v"(pb[1].x), "v"(pb[1].y),
-                 "v"(pb[1].z), "v"(pb[1].w), "v"(pl[0].x), "v"(pl[0].y), "v"(pl[0].z), "v"(pl[0].w), "v"(pl[1].x),
-                 "v"(pl[1].y), "v"(pl[1].z), "v"(pl[1].w), "v"(lsum));
-    // Lazy max: the reference max m_run moves only when a block exceeds it
-    // by more than 8 (log2 units), so weights stay <= 2^8 and O is rarely
-    // rescaled; the result is the same softmax, only the common factor
-    // differs.  The weights above were formed against m_run (each half of
-    // the wave judging its own 16 keys of the query); if the block moves the
-    // max of any query, the halves agree on it, O is rescaled and the
-    // weights are formed again.
+    for (int j = 2; j < 16; ++j) mx = fmaxf(mx, x[j]);
     if (__builtin_amdgcn_ballot_w64(mx * sc > m_run + 8.f) != 0) {
       mx = fmaxf(mx, other_half(mx));
       const float mblk = mx * sc;
       const bool bump = mblk > m_run + 8.f;
       const float m_new = bump ? mblk : m_run;
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = bump ? fast_exp2(m_run - m_use) : 1.f;
+      const float alpha = bump ? fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new)) : 1.f;
       l_run *= alpha;
       m_run = m_new;
 #pragma unroll
       for (int dt = 0; dt < kPfD / 32; ++dt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
-      lsum = 0.f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) weigh_pair(x, m_use, q, lsum, pb, pl);
     }
-    l_run += lsum;
+    const float m = (m_run == -INFINITY) ? 0.f : m_run;
+    const Rows nr = rows(h + 3);
+    const bool more = h + 3 < nkb;  // block h+3 exists: load it
+    uint4 ka[kPfD / 16], va[2][kPfD / 32], pb[2], pl[2];
+    float p[16], lsum = 0.f;
+    // Pair q (registers 2q, 2q+1): the two weights, then their packing.
+    auto exps = [&](int q) __attribute__((always_inline)) {
+      p[2 * q] = fast_exp2(fmaf(x[2 * q], sc, -m));
+      p[2 * q + 1] = fast_exp2(fmaf(x[2 * q + 1], sc, -m));
+      lsum += p[2 * q];
+      lsum += p[2 * q + 1];
+    };
+    auto pack = [&](int q) __attribute__((always_inline)) {
+      const float p0 = p[2 * q], p1 = p[2 * q + 1];
+      uint32_t hw, lw = 0;
+      if constexpr (T == Dt::BF16) {
+        const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+        hw = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // high halves: p1 | p0
+        lw = pack_pair<true>(p0 - __uint_as_float(b0 & 0xffff0000u), p1 - __uint_as_float(b1 & 0xffff0000u));
+      } else {
+        hw = pack_pair<false>(p0, p1);
+      }
+      const int t = q / 4, e = q % 4;
+      if (e == 0) { pb[t].x = hw; pl[t].x = lw; }
+      else if (e == 1) { pb[t].y = hw; pl[t].y = lw; }
+      else if (e == 2) { pb[t].z = hw; pl[t].z = lw; }
+      else { pb[t].w = hw; pl[t].w = lw; }
+    };
+    constexpr int kHalf = kPV / 2;       // PV MFMAs per key half
+    constexpr int kPer = kHalf / 4;      // slots per pair while the first half runs
+    ka[0] = kread(ks, 0);
+    ka[1] = kread(ks, 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int n = 0; n < kPV; ++n) {
-      pv(n, va, pb, pl);
-      if (n == 0 && h + 3 < nkb) issue_half(nr, 0, ds);
-      if (n == 2 && h + 3 < nkb) issue_half(nr, 1, ds);
+    for (int sl = 0; sl < 8 + kPV; ++sl) {
+      if (sl < 8) {
+        snext = mfma<T>(ka[sl], qf[sl], sl == 0 ? f32x16{} : snext);
+        if (sl + 2 < 8) ka[sl + 2] = kread(ks, sl + 2);
+        va[sl / 4][sl % 4] = vread(vs, sl / 4, sl % 4);
+        if (sl % 2 == 0) exps(sl / 2);
+        else pack(sl / 2);
+      } else {
+        pv(sl - 8, va, pb, pl);
+        if (sl < 8 + kHalf) {
+          const int local = sl - 8, q = 4 + local / kPer;
+          if (kPer == 1 || local % kPer == 0) exps(q);
+          if (kPer == 1 || local % kPer == 1) pack(q);
+        }
+        if (more && sl == 8 + kHalf) issue_half(nr, 0, ds);
+        if (more && sl == 8 + kHalf + 2) issue_half(nr, 1, ds);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
+    l_run += lsum;
   };
   auto step = [&](int h, f32x16 &scur, f32x16 &snext, auto vs, auto ks, auto ds) __attribute__((always_inline)) {
     if (h < wave_nkb) compute(h, scur, snext, vs, ks, ds);
