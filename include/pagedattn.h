@@ -233,6 +233,29 @@ pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32
                                            int64_t num_blocks, float scale, pa_dtype dtype,
                                            void *stream);
 
+/*
+ * pa_stream_read -- measurement helper, not a step of the attention path.
+ *
+ * Reads `bytes` bytes of device memory once, with 16-byte non-temporal
+ * loads, in `workgroups` workgroups of 256 lanes that sweep the buffer
+ * together in grid-stride order; the kernel does nothing else.  Its rate is the plain streaming
+ * read bandwidth of the device the cache kernels run on, the same-device
+ * reference beside the vendor's HBM figure for memory-bound kernels
+ * (decode reads every valid K/V row once: "Efficient Memory Management for
+ * Large Language Model Serving with PagedAttention", evaluation section).
+ *
+ *  src         device buffer, 16-byte aligned; bytes a positive multiple of
+ *              16.  Read only.
+ *  sink        device uint32 [4 * workgroups]; receives one XOR of the data
+ *              per wave (so the loads cannot be elided).  Caller-owned.
+ *  workgroups  1 .. 2^31-1.
+ *
+ * Errors: PA_ERR_INVALID_ARG for a null or misaligned pointer or a bad size;
+ * PA_ERR_HIP if the launch fails.
+ */
+pa_status pa_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t workgroups,
+                         void *stream);
+
 #ifdef __cplusplus
 }
 #endif

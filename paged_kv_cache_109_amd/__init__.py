@@ -1,13 +1,14 @@
 """libpagedattn: paged KV-cache attention for AMD Instinct MI355X (gfx950).
 
 The computation lives in hand-written HIP kernels behind the C ABI of
-include/pagedattn.h (libpagedattn.so, built by `python -m
-paged_kv_cache_109_amd.build`); this package is the thin Python binding plus
+include/pagedattn.h (libpagedattn.so, built by `python
+paged_kv_cache_109_amd/build.py`); this package is the thin Python binding plus
 host-side slot translation. Importing it fails if the library is not built.
 """
 from ._binding import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
+    STREAM_SINK_WORDS_PER_GROUP,
     PagedAttnError,
     abi_version,
     alloc_decode_workspace,
@@ -19,5 +20,6 @@ from ._binding import (  # noqa: F401
     paged_attention_decode_reduce,
     paged_attention_prefill_chunk,
     reshape_and_cache,
+    stream_read,
 )
 from .slots import slot_mapping  # noqa: F401

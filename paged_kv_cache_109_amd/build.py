@@ -1,6 +1,6 @@
 """Build libpagedattn.so (HIP, gfx950) in-tree.
 
-    python -m paged_kv_cache_109_amd.build
+    python paged_kv_cache_109_amd/build.py
 
 Every source is compiled by hipcc for gfx950 only, with packed-fp32 ops
 disabled, then linked into paged_kv_cache_109_amd/libpagedattn.so.

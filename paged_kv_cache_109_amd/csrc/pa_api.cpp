@@ -362,4 +362,14 @@ pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32
                     "prefill chunk");
 }
 
+pa_status pa_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t workgroups, void *stream) {
+  if (!src || !sink) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (bytes <= 0 || bytes % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG, "bytes %lld is not a positive multiple of 16", (long long)bytes);
+  if (workgroups <= 0) return fail(PA_ERR_INVALID_ARG, "workgroups must be positive");
+  if (!aligned16(src) || !aligned16(sink)) return fail(PA_ERR_INVALID_ARG, "src and sink must be 16-byte aligned");
+  return hip_status(pa::launch_stream_read(src, bytes, sink, workgroups, reinterpret_cast<hipStream_t>(stream)),
+                    "stream read");
+}
+
 }  // extern "C"

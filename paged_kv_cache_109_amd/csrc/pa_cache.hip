@@ -128,4 +128,44 @@ hipError_t launch_copy_blocks(void *const *k_caches, void *const *v_caches, int3
   return hipSuccess;
 }
 
+// ---------------------------------------------------------- streaming read
+//
+// The bandwidth reference the cache kernels are compared with on the same
+// device: a read of one contiguous buffer with 16-byte non-temporal loads and
+// nothing else.  The workgroups sweep the buffer together in grid-stride
+// order, each lane with four loads in flight.  Every lane XORs what it read
+// and each wave stores the XOR of its lanes, so no load can be dropped.
+
+constexpr int kStreamUnroll = 4;
+static_assert(kStreamSinkWordsPerGroup == kCacheThreads / 64, "one sink word per wave");
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kCacheThreads) void stream_read_kernel(const u32x4 *__restrict__ src, int64_t n16,
+                                                                    uint32_t *__restrict__ sink) {
+  constexpr int64_t kSpan = (int64_t)kCacheThreads * kStreamUnroll;
+  const int64_t stride = (int64_t)gridDim.x * kSpan;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  int64_t base = (int64_t)blockIdx.x * kSpan + threadIdx.x;
+  for (; base + (kStreamUnroll - 1) * kCacheThreads < n16; base += stride) {
+    u32x4 r[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) r[u] = __builtin_nontemporal_load(src + base + u * kCacheThreads);
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) acc ^= r[u];
+  }
+  // The last, partial span of the sweep: at most kStreamUnroll - 1 loads.
+  for (; base < n16; base += kCacheThreads) acc ^= __builtin_nontemporal_load(src + base);
+  uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x ^= __shfl_xor(x, m);
+  if ((threadIdx.x & 63) == 0) sink[(int64_t)blockIdx.x * kStreamSinkWordsPerGroup + threadIdx.x / 64] = x;
+}
+
+hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t workgroups,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)workgroups), dim3(kCacheThreads), 0, stream,
+                     reinterpret_cast<const u32x4 *>(src), bytes / 16, sink);
+  return hipGetLastError();
+}
+
 }  // namespace pa

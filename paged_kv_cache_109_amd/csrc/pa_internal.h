@@ -57,6 +57,11 @@ hipError_t launch_copy_blocks(void *const *k_caches, void *const *v_caches, int3
                               const int64_t *block_mapping, int64_t num_pairs, int64_t block_bytes,
                               int64_t num_blocks, hipStream_t stream);
 
+// Sink words the streaming-read kernel stores per workgroup (one per wave).
+constexpr int kStreamSinkWordsPerGroup = 4;
+hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t workgroups,
+                              hipStream_t stream);
+
 struct PrefillArgs {
   void *out;                    // [total_q][H][D]
   const void *q;                // [total_q][H][D]

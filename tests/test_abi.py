@@ -106,3 +106,13 @@ def test_prefill_rejects_non_positive_scale(scale):
     # so the call must fail before anything is launched.
     f = B._lib.pa_paged_attention_prefill_chunk
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 10, 5, 100, 4, 128, 16, 64, scale, 2, None) == 1
+
+
+def test_stream_read_rejects_bad_arguments():
+    f = B._lib.pa_stream_read
+    assert f(None, 4096, FAKE, 8, None) == 1
+    assert f(FAKE, 4096, None, 8, None) == 1
+    assert f(FAKE, 4100, FAKE, 8, None) == 1
+    assert f(FAKE, 0, FAKE, 8, None) == 1
+    assert f(FAKE, 4096, FAKE, 0, None) == 1
+    assert f(FAKE + 8, 4096, FAKE, 8, None) == 1

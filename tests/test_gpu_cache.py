@@ -130,3 +130,18 @@ def test_parallel_sampling_copy_across_40_layers():
         bits = a.view(torch.int16)
         assert torch.equal(bits[dst_t], s_before)
         assert torch.equal(bits[keep_t], keep_before)
+
+
+@pytest.mark.parametrize("words16,groups", [(1, 1), (1, 8), (259, 7), (65536 + 3, 300), (1 << 20, 2048)])
+def test_stream_read_reads_every_word(words16, groups):
+    # The XOR of the per-wave sink words is the XOR of every 32-bit word of
+    # the buffer exactly when each 16-byte chunk was read once.
+    rng = np.random.default_rng(words16 + groups)
+    data = rng.integers(0, 2**32, size=4 * words16, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(data.view(np.int32)).cuda()
+    sink = torch.zeros(4 * groups, dtype=torch.int32, device="cuda")
+    say(f"  stream_read {16 * words16} B, {groups} workgroups")
+    pa.stream_read(buf, sink, groups)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(data)
