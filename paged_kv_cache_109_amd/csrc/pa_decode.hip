@@ -187,31 +187,35 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 }
 
 // Batches of at most kSelfPlanSeqs sequences: every worker wave reads all
-// context lengths (one chunk of 64 per VGPR, all loads issued at once),
-// prefix-sums the tile counts across lanes, and finds the (s, h, t) of its
-// first tile itself -- no plan launch.  Wave 0 also publishes T and G in
-// plan[0..1]; every worker stores its start for the fix-up, and zeroes the
-// outputs of the empty sequences s with s % G == w.  Returns false if the
-// wave has no work.
+// context lengths and finds the (s, h, t) of its first tile itself -- no plan
+// launch.  Lane l owns the k = ceil(S / 64) consecutive sequences from l*k, so
+// one inclusive scan over the lanes' tile counts places every lane's run in
+// the stream; the lane whose run holds tile g0 is found with a ballot and its
+// k sequences are walked on the scalar unit.  Wave 0 also publishes T and G
+// in plan[0..1]; every worker stores its start for the fix-up, and zeroes
+// the outputs of the empty sequences s with s % G == w.  Returns false if
+// the wave has no work.
 __device__ __forceinline__ bool self_plan(const DecodeArgs &a, uint32_t w, uint32_t &total, uint32_t &G,
                                           int &s0, int &h0, int &t0) {
-  constexpr int kChunks = kSelfPlanSeqs / kWave;
+  constexpr int kMaxPerLane = kSelfPlanSeqs / kWave;
   const int lane = threadIdx.x % kWave;
   const uint32_t H = (uint32_t)a.num_heads;
   const int S = a.num_seqs;
-  int32_t raw[kChunks];
+  const int k = (S + kWave - 1) / kWave;  // wave-uniform, 1 .. kMaxPerLane
+  const int first = lane * k;
+  int32_t raw[kMaxPerLane];
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) raw[c] = a.context_lens[min(c * kWave + lane, S - 1)];
-  uint32_t tiles[kChunks];
-  total = 0;
+  for (int i = 0; i < kMaxPerLane; ++i)
+    if (i < k) raw[i] = a.context_lens[min(first + i, S - 1)];
+  uint32_t tiles[kMaxPerLane];
+  uint32_t mine = 0;
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    tiles[c] = c * kWave + lane < S ? (uint32_t)tiles_of(clip_ctx(raw[c], a.ctx_cap)) : 0u;
-    uint32_t x = tiles[c] * H;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off, kWave);
-    total += __builtin_amdgcn_readfirstlane(x);
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    tiles[i] = (i < k && first + i < S) ? (uint32_t)tiles_of(clip_ctx(raw[i], a.ctx_cap)) : 0u;
+    mine += tiles[i] * H;
   }
+  const uint32_t incl = wave_inclusive_scan(mine);
+  total = __builtin_amdgcn_readlane(incl, kWave - 1);
   G = total < (uint32_t)a.workers ? total : (uint32_t)a.workers;
   if (w == 0 && lane == 0) {
     a.plan[0] = total;
@@ -221,32 +225,30 @@ __device__ __forceinline__ bool self_plan(const DecodeArgs &a, uint32_t w, uint3
   const uint32_t zero_waves = G > 0 ? G : 1u;
   if (w < zero_waves) {
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const int s = c * kWave + lane;
-      uint64_t todo = __builtin_amdgcn_ballot_w64(s < S && tiles[c] == 0 && (uint32_t)s % zero_waves == w);
+    for (int i = 0; i < kMaxPerLane; ++i) {
+      if (i >= k) break;
+      const int s = first + i;
+      uint64_t todo = __builtin_amdgcn_ballot_w64(s < S && tiles[i] == 0 && (uint32_t)s % zero_waves == w);
       while (todo) {
         const int l = __builtin_ctzll(todo);
         todo &= todo - 1;
         uint4 *row = reinterpret_cast<uint4 *>(reinterpret_cast<uint32_t *>(a.out) +
-                                               (int64_t)(c * kWave + l) * a.out_row_words);
-        for (int i = lane; i < a.out_row_words / 4; i += kWave) row[i] = make_uint4(0, 0, 0, 0);
+                                               (int64_t)(l * k + i) * a.out_row_words);
+        for (int j = lane; j < a.out_row_words / 4; j += kWave) row[j] = make_uint4(0, 0, 0, 0);
       }
     }
   }
   if (w >= G) return false;
   const uint32_t g0 = range_begin(w, total, G);
-  uint32_t before = 0;  // tiles of the chunks already passed
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > g0);
+  const int l = __builtin_ctzll(hit);  // first lane whose run passes g0 (exists: g0 < total)
+  uint32_t start = __builtin_amdgcn_readlane(incl - mine, l);
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const uint32_t v = tiles[c] * H;
-    const uint32_t incl = before + wave_inclusive_scan(v);
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > g0);
-    if (hit != 0) {
-      const int l = __builtin_ctzll(hit);  // first lane whose range passes g0
-      const uint32_t ts = __builtin_amdgcn_readlane(tiles[c], l);
-      const uint32_t start = __builtin_amdgcn_readlane(incl - v, l);
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const uint32_t ts = __builtin_amdgcn_readlane(tiles[i], l);
+    if (i < k && g0 < start + ts * H) {
       const uint32_t local = g0 - start;
-      s0 = c * kWave + l;
+      s0 = l * k + i;
       h0 = (int)(local / ts);
       t0 = (int)(local % ts);
       if (lane == 0) {
@@ -255,9 +257,38 @@ __device__ __forceinline__ bool self_plan(const DecodeArgs &a, uint32_t w, uint3
       }
       return true;
     }
-    before = __builtin_amdgcn_readlane(incl, kWave - 1);
+    start += ts * H;
   }
-  return false;  // not reached: g0 < total
+  return false;  // not reached: lane l's run holds g0
+}
+
+// First worker whose range holds tiles of a pair starting at pair_start: the
+// last w with range_begin(w) <= pair_start.
+__device__ __forceinline__ uint32_t first_worker(uint32_t pair_start, uint32_t total, uint32_t G) {
+  return (uint32_t)((((uint64_t)pair_start + 1) * G + total - 1) / total) - 1;
+}
+
+// Merge the fragments workers wa..wb left for pair (s, h) and write its
+// output row: wa's is in its back slot (1), every later worker's in its front
+// slot (0).  One wave; lanes stride over the head dimension.
+template <Dt T, int D>
+__device__ __forceinline__ void merge_fragments(const DecodeArgs &a, uint32_t wa, uint32_t wb, int s, int h) {
+  const int lane = threadIdx.x % kWave;
+  auto frag = [&](uint32_t v) -> const float * {
+    return a.frags + ((int64_t)v * 2 + (v == wa ? 1 : 0)) * (D + 2);
+  };
+  float M = -INFINITY;
+  for (uint32_t v = wa; v <= wb; ++v) M = fmaxf(M, frag(v)[D]);
+  const float mu = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f;
+  for (uint32_t v = wa; v <= wb; ++v) L += frag(v)[D + 1] * fast_exp2(frag(v)[D] - mu);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int64_t out_row = ((int64_t)s * a.num_heads + h) * D;
+  for (int d = lane; d < D; d += kWave) {
+    float A = 0.f;
+    for (uint32_t v = wa; v <= wb; ++v) A += frag(v)[d] * fast_exp2(frag(v)[D] - mu);
+    store_out_elem<T, D>(a.out, out_row + d, A * inv);
+  }
 }
 
 template <Dt T, int D, int B>
@@ -452,6 +483,7 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_
       refill(d);
     }
   }
+
 }
 
 // Merge the fragments of every pair cut by range boundaries.  Worker wave w
@@ -461,7 +493,6 @@ template <Dt T, int D>
 __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_reduce_kernel(DecodeArgs a) {
   // Every worker wave v that the loop below visits has a non-empty range
   // (the plan never uses more workers than tiles) and wrote its fragment.
-  const int lane = threadIdx.x % kWave;
   const uint32_t G = a.plan[1];
   const uint32_t w = blockIdx.x * kDecodeWavesPerGroup + wave_id_uniform();
   if (w >= G) return;
@@ -474,24 +505,7 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_reduce_ker
   const uint32_t nt = (uint32_t)tiles_of(clip_ctx(a.context_lens[s], a.ctx_cap));
   const uint32_t pair_start = g0 - t;
   if (pair_start + nt > g1) return;  // continues past this range: a later worker merges it
-  // First worker holding the pair: the last w' with range_begin(w') <= pair_start.
-  const uint32_t wa = (uint32_t)((((uint64_t)pair_start + 1) * G + total - 1) / total) - 1;
-
-  auto frag = [&](uint32_t v) -> const float * {
-    return a.frags + ((int64_t)v * 2 + (v == wa ? 1 : 0)) * (D + 2);
-  };
-  float M = -INFINITY;
-  for (uint32_t v = wa; v <= w; ++v) M = fmaxf(M, frag(v)[D]);
-  const float mu = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f;
-  for (uint32_t v = wa; v <= w; ++v) L += frag(v)[D + 1] * fast_exp2(frag(v)[D] - mu);
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  const int64_t out_row = ((int64_t)s * a.num_heads + h) * D;
-  for (int d = lane; d < D; d += kWave) {
-    float A = 0.f;
-    for (uint32_t v = wa; v <= w; ++v) A += frag(v)[d] * fast_exp2(frag(v)[D] - mu);
-    store_out_elem<T, D>(a.out, out_row + d, A * inv);
-  }
+  merge_fragments<T, D>(a, first_worker(pair_start, total, G), w, s, h);
 }
 
 // ------------------------------------------------------------------ dispatch

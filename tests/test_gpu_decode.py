@@ -145,6 +145,45 @@ def test_split_calls_equal_the_fused_call_on_a_side_stream():
     assert torch.equal(fused.view(torch.int16), out.view(torch.int16))
 
 
+@pytest.mark.parametrize("S", [63, 64, 65, 130, 1000, 1024, 1025])
+@pytest.mark.parametrize("workers", [0, 37])
+def test_batch_sizes_around_the_plan_layouts(S, workers):
+    """Up to 1024 sequences the worker waves plan for themselves, each lane
+    owning ceil(S/64) consecutive sequences; above that a plan kernel runs.
+    Short ragged contexts, a fifth of them empty, at batch sizes on both
+    sides of every layout change."""
+    rng = np.random.default_rng(S)
+    lens = rng.integers(0, 41, size=S)
+    lens[rng.random(S) < 0.2] = 0
+    c = W.make_decode_case(S, 2, 64, 16, "bf16", [int(x) for x in lens], seed=S, max_blocks_per_seq=3)
+    dc = DeviceCase(c)
+    check_attention(gpu_decode(dc, workers), ref_decode(c), "bf16", f"S={S} workers={workers}")
+
+
+def test_one_workspace_over_changing_splits():
+    """Calls with different worker counts (so different plans and cut points)
+    share one workspace: each must equal the two-pass result bit for bit and
+    match the oracle, whatever an earlier call left in the workspace."""
+    c = W.make_decode_case(6, 4, 128, 16, "f16", [1, 47, 300, 1024, 1500, 2048], seed=3, max_blocks_per_seq=128)
+    dc = DeviceCase(c)
+    ref = ref_decode(c)
+    ws = pa.alloc_decode_workspace(6, 4, 128, c.max_context_len, 16)
+    ws2 = pa.alloc_decode_workspace(6, 4, 128, c.max_context_len, 16)
+    for split in [3, 64, 0, 17, 1000, 5, 0, 2]:
+        say(f"  decode on a shared workspace, split_workers={split}")
+        out = torch.empty_like(dc.q)
+        pa.paged_attention_decode(out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
+                                  c.max_context_len, c.scale, workspace=ws, split_workers=split)
+        two = torch.empty_like(dc.q)
+        pa.paged_attention_decode_partitions(two, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
+                                             c.max_context_len, c.scale, workspace=ws2, split_workers=split)
+        pa.paged_attention_decode_reduce(two, dc.context_lens, c.max_context_len, c.max_blocks_per_seq, 4, 128, 16,
+                                         workspace=ws2, split_workers=split)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), two.view(torch.int16)), f"split {split}"
+        check_attention(out, ref, "f16", f"split {split}")
+
+
 # ------------------------------------------------------------ full-size workloads
 
 def test_opt13b_batch64_full_size():
