@@ -9,10 +9,15 @@ describes): write each sequence's new K/V into its cache slot
 cache (decode partition pass + reduce pass). Inputs are seeded synthetic
 tensors of the workload's shapes, resident in HBM before timing starts.
 
+The timed steps are eager launches of the step's kernels with nothing else
+between the two events that bracket them. --graph replays the step captured
+once as a HIP graph instead (one graph per pool replica: the same kernels on
+the same buffers); on ROCm 7 that measured slower than eager launches.
+
 Prints ONE JSON line. `value` is decode tokens/s for one layer call (one
 query token per sequence per step). `roofline` is for the dominant kernel,
 the decode partition pass, whose launches are bracketed by HIP events on the
-stream they run on. `cpu_baseline` times the CPU oracle (test
+stream they run on, in a separate eager pass. `cpu_baseline` times the CPU oracle (test
 infrastructure, never tuned) on the same batch on the host cores.
 """
 from __future__ import annotations
@@ -44,6 +49,8 @@ def parse():
                     help="copies of the KV pool used in turn, so no step finds the last one's data in cache")
     ap.add_argument("--split-workers", type=int, default=0,
                     help="worker waves the tile stream is cut among (0: as many as the GPU holds)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured as a HIP graph instead of eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-runs", type=int, default=3)
     return ap.parse_args()
@@ -105,6 +112,45 @@ def measure_stream_read(torch, pa, dev, gib: int = 4):
     print(f"[bench] streaming read {best['gbps']:.0f} GB/s ({best['workgroups']} workgroups)", file=sys.stderr,
           flush=True)
     return best
+
+
+def capture_steps(torch, step, n):
+    """One HIP graph per pool replica of the whole step (torch.cuda.graph):
+    the same kernels on the same buffers, launched as one graph. Warmed up
+    eagerly on a side stream first, as torch asks."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(n):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def timed_steps(torch, step, args, n_replicas):
+    """Warm-up, then args.steps steps between two events on the launch stream
+    (synchronised before and after), with nothing else in the timed region.
+    Returns (ms per step, how the step was launched)."""
+    graphs = capture_steps(torch, step, n_replicas) if args.graph else None
+    run = (lambda i: graphs[i % n_replicas].replay()) if graphs else step
+    for i in range(args.warmup):
+        run(i)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        run(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / args.steps, ("hip graph replay" if graphs else "eager launches")
 
 
 def launch_stats(ms):
@@ -187,15 +233,13 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    ms_per_step, launch = timed_steps(torch, step, args, len(pools))
+    # Per-kernel durations from a separate eager pass with events between the
+    # kernels (kept out of the timed region above).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
     for i in range(args.steps):
         step(i, evs[i])
-    end.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
     part_ms = [e[1].elapsed_time(e[2]) for e in evs]
     part_avg_s = float(np.mean(part_ms)) * 1e-3
     pre_avg_s = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
@@ -281,6 +325,7 @@ def main():
         "config": {"workload": case.name, "num_seqs": S, "num_heads": H, "head_dim": D, "block_size": B,
                    "context_tokens": int(case.context_lens.sum()), "max_context_len": max_ctx,
                    "split_workers": workers or pa.decode_default_workers(tdt, D, B), "pool_replicas": args.replicas,
+                   "step_launch": launch,
                    "step": ("copy_blocks(CoW pairs) + " if copies else "")
                    + ("reshape_and_cache(new tokens) + " if writes else "") + "decode partitions + decode reduce"},
         "effective_kv_gbps": kv_bytes / (ms_per_step * 1e-3) / 1e9,
@@ -343,15 +388,12 @@ def bench_prefill(args):
 
     for i in range(args.warmup):
         step(i)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record(stream)
+    ms_per_step, launch = timed_steps(torch, step, args, len(pools))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
         step(i, evs[i])
-    end.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
     kern_ms = [a.elapsed_time(b) for a, b in evs]
     kern_s = float(np.mean(kern_ms)) * 1e-3
     # Causal work: query j of a sequence with c cached tokens sees c + j + 1
@@ -383,7 +425,7 @@ def bench_prefill(args):
         "config": {"workload": case.name, "num_seqs": S, "q_len": max_q, "num_heads": H, "head_dim": D,
                    "block_size": B, "context_tokens": int(case.context_lens.sum()),
                    "step": "reshape_and_cache(4096 chunk tokens) + prefill chunk kernel",
-                   "pool_replicas": len(pools)},
+                   "pool_replicas": len(pools), "step_launch": launch},
         "stream_read": stream_read,
         "roofline": {"bound": "hbm", "kernel": "prefill_chunk_kernel", "achieved": gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
