@@ -57,14 +57,15 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, misalignment, inconsistent sizes */
   PA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, block_size or dtype */
   PA_ERR_WORKSPACE = 3,   /* decode workspace missing or too small */
-  PA_ERR_HIP = 4          /* a kernel launch failed */
+  PA_ERR_HIP = 4,         /* a kernel launch failed */
+  PA_ERR_NO_BLOCKS = 5    /* block manager: the free pool cannot cover the request */
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -255,6 +256,79 @@ pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32
  */
 pa_status pa_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t workgroups,
                          void *stream);
+
+/* ------------------------------------------------------------------------
+ * Block manager (host only; no device memory, no GPU calls).
+ *
+ * The bookkeeping that feeds the kernels above: a pool of num_blocks
+ * physical blocks of block_size tokens, one block table per sequence, one
+ * reference count per block.  It follows the paper notes' KV cache manager
+ * and its three operations ("PagedAttention: Efficient Memory Management for
+ * Large Language Model Serving", sections 3.2, 3.4.1, 3.4.2 and 4.2: fork,
+ * append, free) and the copy-on-write and block-return walk-throughs of
+ * "KV 캐시 관리와 PagedAttention" (sections on splitting a shared block that
+ * must be written and on returning blocks after a request ends):
+ *  - blocks come from a first-in first-out queue of free blocks (the vLLM
+ *    teardown on arcyou.ai, section on paging the KV cache) whose initial
+ *    order is free_order (NULL: 0, 1, 2, ...); freed blocks join its back;
+ *  - a sequence takes a new block only when its last block is full;
+ *  - fork shares every block of the parent (each gains one reference);
+ *  - appending to a sequence whose partly filled last block is shared moves
+ *    the sequence onto a fresh block and reports (src, dst): the caller must
+ *    copy the block on the device (pa_copy_blocks) before writing the token
+ *    (pa_reshape_and_cache at the returned slot);
+ *  - free drops one reference per block; blocks reaching zero are queued.
+ * Slots are block * block_size + offset, positions count from 0.  A manager
+ * is not thread-safe; every call on it must come from one thread at a time.
+ * Errors change nothing: PA_ERR_INVALID_ARG (null pointer, dead or repeated
+ * sequence id, a table row that would overflow), PA_ERR_NO_BLOCKS.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* A manager over num_blocks blocks (< 2^31); free_order, if not NULL, is a
+ * host array listing every block id once.  *out is NULL on error. */
+pa_status pa_bm_create(int64_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                       const int32_t *free_order, pa_block_manager **out);
+void pa_bm_destroy(pa_block_manager *bm);
+
+/* Free blocks (-1 for a NULL manager) and a block's reference count (-1 if
+ * out of range). */
+int64_t pa_bm_num_free(const pa_block_manager *bm);
+int32_t pa_bm_refcount(const pa_block_manager *bm, int64_t block);
+
+/* A new sequence holding num_tokens tokens (a prompt): ceil(num_tokens /
+ * block_size) blocks at once.  Ids count up from 0 and are never reused. */
+pa_status pa_bm_add_sequence(pa_block_manager *bm, int32_t num_tokens, int32_t *seq_id);
+
+/* A new sequence sharing every block (and the length) of `parent`. */
+pa_status pa_bm_fork(pa_block_manager *bm, int32_t parent, int32_t *child);
+
+/* One more token for each of the num_seqs distinct sequences seqs[i],
+ * handled in order: slots[i] receives the slot of sequence i's new token,
+ * copies[2k], copies[2k+1] the k-th (src, dst) block copy the writes need
+ * first (at most num_seqs), *num_copies their number.  All host arrays.
+ * Either every sequence gets its token or (PA_ERR_NO_BLOCKS when the pool
+ * is short) nothing changes. */
+pa_status pa_bm_append_slots(pa_block_manager *bm, const int32_t *seqs, int32_t num_seqs,
+                             int64_t *slots, int64_t *copies, int32_t *num_copies);
+
+/* End a sequence; blocks no longer referenced return to the free queue. */
+pa_status pa_bm_free_sequence(pa_block_manager *bm, int32_t seq);
+
+/* Length (tokens) and blocks of a live sequence. */
+pa_status pa_bm_sequence(const pa_block_manager *bm, int32_t seq, int32_t *length,
+                         int32_t *num_blocks);
+
+/* The decode inputs of a batch: tables (host int32 [num_seqs][
+ * max_blocks_per_seq], rows padded with -1) and context_lens (host int32
+ * [num_seqs]). */
+pa_status pa_bm_block_tables(const pa_block_manager *bm, const int32_t *seqs, int32_t num_seqs,
+                             int32_t *tables, int32_t *context_lens);
+
+/* Slots (host int64 [count]) of positions first .. first+count-1 of a live
+ * sequence, e.g. its prompt for pa_reshape_and_cache. */
+pa_status pa_bm_slots(const pa_block_manager *bm, int32_t seq, int32_t first, int32_t count,
+                      int64_t *slots);
 
 #ifdef __cplusplus
 }

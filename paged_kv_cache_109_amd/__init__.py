@@ -6,8 +6,10 @@ paged_kv_cache_109_amd/build.py`); this package is the thin Python binding plus
 host-side slot translation. Importing it fails if the library is not built.
 """
 from ._binding import (  # noqa: F401
+    BlockManager,
     EXPORTED,
     LIB_PATH,
+    OutOfBlocks,
     STREAM_SINK_WORDS_PER_GROUP,
     PagedAttnError,
     abi_version,

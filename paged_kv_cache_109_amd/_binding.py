@@ -43,6 +43,17 @@ _SIGS = {
     "pa_paged_attention_prefill_chunk": (
         [P, P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, P], ctypes.c_int),
     "pa_stream_read": ([P, i64, P, i32, P], ctypes.c_int),
+    "pa_bm_create": ([i64, i32, i32, P, P], ctypes.c_int),
+    "pa_bm_destroy": ([P], None),
+    "pa_bm_num_free": ([P], i64),
+    "pa_bm_refcount": ([P, i64], i32),
+    "pa_bm_add_sequence": ([P, i32, P], ctypes.c_int),
+    "pa_bm_fork": ([P, i32, P], ctypes.c_int),
+    "pa_bm_append_slots": ([P, P, i32, P, P, P], ctypes.c_int),
+    "pa_bm_free_sequence": ([P, i32], ctypes.c_int),
+    "pa_bm_sequence": ([P, i32, P, P], ctypes.c_int),
+    "pa_bm_block_tables": ([P, P, i32, P, P], ctypes.c_int),
+    "pa_bm_slots": ([P, i32, i32, i32, P], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -50,7 +61,7 @@ for _name, (_args, _res) in _SIGS.items():
     _fn.restype = _res
 
 EXPORTED = tuple(_SIGS)
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_NO_BLOCKS = range(6)
 _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 
@@ -249,3 +260,96 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int, stream=N
         raise ValueError("sink must be int32 with 4 words per workgroup")
     _check(_lib.pa_stream_read(_dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(sink, "sink"),
                                int(workgroups), _stream(stream)), "stream_read")
+
+
+class OutOfBlocks(PagedAttnError):
+    """The block manager's free pool cannot cover the request (nothing changed)."""
+
+
+def _bm_check(status: int, fn: str) -> None:
+    if status == PA_ERR_NO_BLOCKS:
+        raise OutOfBlocks(status, fn)
+    _check(status, fn)
+
+
+class BlockManager:
+    """The library's host-side block manager (pa_bm_* in include/pagedattn.h):
+    a pool of num_blocks blocks of block_size tokens, per-sequence block
+    tables, reference counts, fork / append / free with copy-on-write.
+    Arrays returned are numpy, ready to upload for the kernels."""
+
+    def __init__(self, num_blocks: int, block_size: int, max_blocks_per_seq: int, free_order=None):
+        import numpy as np
+        self._np = np
+        self.num_blocks, self.block_size, self.max_blocks_per_seq = int(num_blocks), int(block_size), \
+            int(max_blocks_per_seq)
+        order = None
+        if free_order is not None:
+            self._order = np.ascontiguousarray(free_order, dtype=np.int32)
+            if self._order.shape != (self.num_blocks,):
+                raise ValueError("free_order must list every block once")
+            order = self._order.ctypes.data
+        h = ctypes.c_void_p()
+        _check(_lib.pa_bm_create(self.num_blocks, self.block_size, self.max_blocks_per_seq, order,
+                                 ctypes.byref(h)), "pa_bm_create")
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            _lib.pa_bm_destroy(h)
+            self._h = None
+
+    def num_free(self) -> int:
+        return int(_lib.pa_bm_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(_lib.pa_bm_refcount(self._h, int(block)))
+
+    def add_sequence(self, num_tokens: int) -> int:
+        sid = ctypes.c_int32()
+        _bm_check(_lib.pa_bm_add_sequence(self._h, int(num_tokens), ctypes.byref(sid)), "pa_bm_add_sequence")
+        return sid.value
+
+    def fork(self, parent: int) -> int:
+        sid = ctypes.c_int32()
+        _bm_check(_lib.pa_bm_fork(self._h, int(parent), ctypes.byref(sid)), "pa_bm_fork")
+        return sid.value
+
+    def append_slots(self, seqs):
+        """One token for each sequence: (slots int64 [n], copies int64 [k, 2])."""
+        np = self._np
+        ids = np.ascontiguousarray(seqs, dtype=np.int32)
+        n = int(ids.size)
+        slots = np.empty(n, np.int64)
+        copies = np.empty((max(n, 1), 2), np.int64)
+        nc = ctypes.c_int32()
+        _bm_check(_lib.pa_bm_append_slots(self._h, ids.ctypes.data, n, slots.ctypes.data, copies.ctypes.data,
+                                          ctypes.byref(nc)), "pa_bm_append_slots")
+        return slots, copies[:nc.value].copy()
+
+    def free_sequence(self, seq: int) -> None:
+        _bm_check(_lib.pa_bm_free_sequence(self._h, int(seq)), "pa_bm_free_sequence")
+
+    def sequence(self, seq: int):
+        """(length in tokens, number of blocks) of a live sequence."""
+        n, b = ctypes.c_int32(), ctypes.c_int32()
+        _bm_check(_lib.pa_bm_sequence(self._h, int(seq), ctypes.byref(n), ctypes.byref(b)), "pa_bm_sequence")
+        return n.value, b.value
+
+    def block_tables(self, seqs):
+        """(tables int32 [n, max_blocks_per_seq] padded with -1, context_lens int32 [n])."""
+        np = self._np
+        ids = np.ascontiguousarray(seqs, dtype=np.int32)
+        n = int(ids.size)
+        tables = np.empty((n, self.max_blocks_per_seq), np.int32)
+        lens = np.empty(n, np.int32)
+        _bm_check(_lib.pa_bm_block_tables(self._h, ids.ctypes.data, n, tables.ctypes.data, lens.ctypes.data),
+                  "pa_bm_block_tables")
+        return tables, lens
+
+    def slots(self, seq: int, first: int, count: int):
+        np = self._np
+        out = np.empty(int(count), np.int64)
+        _bm_check(_lib.pa_bm_slots(self._h, int(seq), int(first), int(count), out.ctypes.data), "pa_bm_slots")
+        return out

@@ -40,6 +40,16 @@ pa_status hip_status(hipError_t e, const char *what) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+}  // namespace
+
+// The last-error record, for the host-side parts in other files.
+namespace pa {
+pa_status record_error(pa_status st, const char *msg) { return fail(st, "%s", msg); }
+pa_status record_ok() { return ok(); }
+}  // namespace pa
+
+namespace {
+
 int elt_bytes(pa_dtype dt) { return dt == PA_F32 ? 4 : 2; }
 
 bool valid_dtype(int dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
@@ -169,6 +179,7 @@ const char *pa_status_string(pa_status status) {
     case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP launch failure";
+    case PA_ERR_NO_BLOCKS: return "not enough free blocks";
   }
   return "unknown status";
 }

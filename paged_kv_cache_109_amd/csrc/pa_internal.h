@@ -5,9 +5,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/pagedattn.h"
+
 namespace pa {
 
 enum class Dt : int;
+
+// Set (or clear) the message pa_last_error returns; return `st` (PA_OK).
+pa_status record_error(pa_status st, const char *msg);
+pa_status record_ok();
 
 // Arguments of the decode passes.  Pointers are device pointers.
 struct DecodeArgs {

@@ -30,7 +30,7 @@ def test_every_declared_function_is_exported_and_bound():
 
 def test_abi_version_and_status_strings():
     assert pa.abi_version() == int(re.search(r"#define PA_ABI_VERSION (\d+)", HEADER).group(1))
-    for code in range(5):
+    for code in range(6):
         assert B._lib.pa_status_string(code)
     assert B._lib.pa_status_string(99) == b"unknown status"
 
