@@ -49,6 +49,8 @@ def parse():
                     help="copies of the KV pool used in turn, so no step finds the last one's data in cache")
     ap.add_argument("--split-workers", type=int, default=0,
                     help="worker waves the tile stream is cut among (0: as many as the GPU holds)")
+    ap.add_argument("--block-size", type=int, default=16,
+                    help="tokens per KV block for the decode workloads (4, 8, 16, 32 or 64)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the step captured as a HIP graph instead of eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -174,10 +176,13 @@ def main():
     import workloads as W
 
     if args.workload == "chunked_prefill":
+        if args.block_size != 16:
+            print("the chunked_prefill workload uses 16-token blocks", file=sys.stderr)
+            sys.exit(2)
         return bench_prefill(args)
     t0 = time.time()
     case = {"opt13b_b64": W.opt13b_b64, "large_batch_b256": W.large_batch_b256,
-            "parallel_sampling": W.parallel_sampling}[args.workload]()
+            "parallel_sampling": W.parallel_sampling}[args.workload](block_size=args.block_size)
     print(f"[bench] workload {case.name} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
@@ -256,7 +261,8 @@ def main():
     alg_bytes = kv_bytes + 2 * S * H * D * elt + 4 * nblocks + 4 * S
     achieved = alg_bytes / part_avg_s / 1e9
     tokens_per_s = S / (ms_per_step * 1e-3)
-    traffic = committed_traffic("decode_partition_" + case.name.rsplit("_", 1)[0])
+    # Counter summaries are committed for the 16-token-block workloads only.
+    traffic = committed_traffic("decode_partition_" + case.name.rsplit("_", 1)[0]) if B == 16 else None
 
     # The other kernels of the step, each timed by its own events: algorithmic
     # bytes are what the call must read plus what it must write.
@@ -290,6 +296,32 @@ def main():
         print(f"[bench] copy_blocks {P} pairs x {L} layers: {t_l * 1e6:.1f} us, {L * b1 / t_l / 1e9:.0f} GB/s",
               file=sys.stderr, flush=True)
         del layers, ks, vs
+        # Swapping the same blocks of one layer's K and V out to pinned host
+        # memory and back in (one launch each way), over the host link.
+        host_pool = [torch.empty((P,) + tuple(pools[0][0].shape[1:]), dtype=pools[0][0].dtype, pin_memory=True)
+                     for _ in range(2)]
+        out_map = torch.stack([mapping[:, 0], torch.arange(P, device=dev)], dim=1).contiguous()
+        in_map = torch.stack([torch.arange(P, device=dev), mapping[:, 1]], dim=1).contiguous()
+        srcs = [pools[0][0], pools[0][1]]
+        pa.swap_blocks(srcs, host_pool, out_map)
+        torch.cuda.synchronize()
+        sw = {}
+        for name, a_list, b_list, m in (("out", srcs, host_pool, out_map), ("in", host_pool, srcs, in_map)):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+            for a, z in ev:
+                a.record(stream)
+                pa.swap_blocks(a_list, b_list, m)
+                z.record(stream)
+            torch.cuda.synchronize()
+            sw[name] = float(np.median([a.elapsed_time(z) for a, z in ev])) * 1e-3
+        swap_bytes = 2 * P * blk
+        components["swap_blocks_kernel"] = {
+            "pairs": P, "caches": 2, "bytes_each_way": swap_bytes,
+            "to_host_us": sw["out"] * 1e6, "to_host_gbps": swap_bytes / sw["out"] / 1e9,
+            "from_host_us": sw["in"] * 1e6, "from_host_gbps": swap_bytes / sw["in"] / 1e9}
+        print(f"[bench] swap_blocks {P} blocks x 2 caches: to host {swap_bytes / sw['out'] / 1e9:.1f} GB/s, "
+              f"from host {swap_bytes / sw['in'] / 1e9:.1f} GB/s", file=sys.stderr, flush=True)
+        del host_pool
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -30,9 +30,10 @@
  *    position p of a sequence is block_tables[s][p / B] * B + p % B
  *    ("KV 캐시 관리와 PagedAttention", llm-systems-engineering.pages.dev,
  *    section on linking token order to storage).
- *  - Supported shapes: head_dim 64 or 128; block_size 4, 8, 16 or 32; dtype
- *    fp32, fp16 or bf16 (the prefill chunk: fp16/bf16, head_dim 128).  All
- *    data pointers must be 16-byte aligned.
+ *  - Supported shapes: head_dim 64 or 128; block_size 4, 8, 16, 32 or 64
+ *    (the prefill chunk: 4 to 32); dtype fp32, fp16 or bf16 (the prefill
+ *    chunk: fp16/bf16, head_dim 128).  All data pointers must be 16-byte
+ *    aligned.
  *  - Errors are found by synchronous host checks on the scalar arguments and
  *    pointers (never on device data).  On any error the call returns a
  *    non-zero status, enqueues nothing and writes nothing; pa_last_error()
@@ -233,6 +234,33 @@ pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32
                                            int32_t head_dim, int32_t block_size,
                                            int64_t num_blocks, float scale, pa_dtype dtype,
                                            void *stream);
+
+/*
+ * pa_swap_blocks -- batched whole-block copy between two pools, for swapping
+ * blocks out to host memory and back in (paper notes "PagedAttention:
+ * Efficient Memory Management for Large Language Model Serving", sections
+ * 3.5 Scheduling and Preemption and 4.1 Kernel-level Optimization: blocks
+ * of preempted requests move to CPU memory and are copied in many small
+ * pieces, which one launch replaces).  For every cache c < num_caches and
+ * every pair (src, dst) = (block_mapping[2i], block_mapping[2i+1]) it copies
+ * block src of src_caches[c] (a pool of src_num_blocks blocks) onto block dst
+ * of dst_caches[c] (dst_num_blocks blocks): block_bytes bytes, every head
+ * and slot.
+ *
+ *  src_caches, dst_caches  HOST arrays of num_caches pointers, e.g. the K
+ *                      and V caches of every layer; each is device memory
+ *                      or pinned host memory (hipHostMalloc, torch's
+ *                      pin_memory), checked with hipPointerGetAttributes --
+ *                      pageable memory is refused (PA_ERR_INVALID_ARG).
+ *  block_mapping       int64 [num_pairs][2], device or pinned host memory.
+ *                      Destinations must be distinct within a call; pairs
+ *                      with an index outside its pool are skipped.
+ *  block_bytes         a positive multiple of 16.
+ * Enqueued on `stream`; the caller keeps both pools alive until it ends.
+ */
+pa_status pa_swap_blocks(const void *const *src_caches, void *const *dst_caches, int32_t num_caches,
+                         const int64_t *block_mapping, int64_t num_pairs, int64_t block_bytes,
+                         int64_t src_num_blocks, int64_t dst_num_blocks, void *stream);
 
 /*
  * pa_stream_read -- measurement helper, not a step of the attention path.

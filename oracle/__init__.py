@@ -183,3 +183,22 @@ def copy_blocks(k_caches: Sequence[np.ndarray], v_caches: Sequence[np.ndarray], 
     _check((lib or load()).oracle_copy_blocks(
         ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp, ctypes.c_void_p), L, _ptr(bm),
         bm.shape[0], block_bytes, N))
+
+
+def swap_blocks(src_caches: Sequence[np.ndarray], dst_caches: Sequence[np.ndarray], block_mapping) -> None:
+    """Copy whole blocks from one pool to another, in place: for every cache
+    pair and every (src, dst) pair, block dst of the destination becomes a
+    byte copy of block src of the source (paper notes "PagedAttention:
+    Efficient Memory Management for Large Language Model Serving", sections
+    3.5 and 4.1: blocks of a preempted request move between GPU and CPU
+    memory, many blocks per copy launch). Destinations must be distinct."""
+    bm = np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2)
+    if len(set(bm[:, 1].tolist())) != bm.shape[0]:
+        raise OracleError("bad swap mapping: repeated destination")
+    for src, dst in zip(src_caches, dst_caches):
+        if src.shape[1:] != dst.shape[1:] or src.dtype != dst.dtype:
+            raise OracleError("bad swap: pools of different block shapes")
+        for s, d in bm:
+            if not (0 <= s < src.shape[0] and 0 <= d < dst.shape[0]):
+                raise OracleError("bad swap mapping: block outside its pool")
+            dst[d] = src[s]

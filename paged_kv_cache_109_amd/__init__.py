@@ -23,5 +23,6 @@ from ._binding import (  # noqa: F401
     paged_attention_prefill_chunk,
     reshape_and_cache,
     stream_read,
+    swap_blocks,
 )
 from .slots import slot_mapping  # noqa: F401

@@ -43,6 +43,7 @@ _SIGS = {
     "pa_paged_attention_prefill_chunk": (
         [P, P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, P], ctypes.c_int),
     "pa_stream_read": ([P, i64, P, i32, P], ctypes.c_int),
+    "pa_swap_blocks": ([P, P, i32, P, i64, i64, i64, i64, P], ctypes.c_int),
     "pa_bm_create": ([i64, i32, i32, P, P], ctypes.c_int),
     "pa_bm_destroy": ([P], None),
     "pa_bm_num_free": ([P], i64),
@@ -221,6 +222,36 @@ def copy_blocks(k_caches: Sequence[torch.Tensor], v_caches: Sequence[torch.Tenso
     _check(_lib.pa_copy_blocks(ctypes.cast(kp, P), ctypes.cast(vp, P), L,
                                _dev(block_mapping, "block_mapping", torch.int64), int(block_mapping.shape[0]),
                                block_bytes, N, _stream(stream)), "copy_blocks")
+
+
+def swap_blocks(src_caches: Sequence[torch.Tensor], dst_caches: Sequence[torch.Tensor], block_mapping: torch.Tensor,
+                stream=None) -> None:
+    """For every cache pair and every (src, dst) row of block_mapping (int64
+    [pairs, 2]), copy block src of src_caches[c] onto block dst of
+    dst_caches[c]. Caches are [blocks, heads, block_size, head_dim] device
+    tensors or pinned host tensors (e.g. all layers' K and V). One launch."""
+    C = len(src_caches)
+    if C == 0 or len(dst_caches) != C:
+        raise ValueError("need one destination per source cache")
+    def dims(t):
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError("caches must be contiguous [blocks, heads, block_size, head_dim]")
+        return tuple(t.shape[1:]), t.element_size()
+    shape = dims(src_caches[0])
+    for a, b in zip(src_caches, dst_caches):
+        if dims(a) != shape or dims(b) != shape:
+            raise ValueError("all caches must share [heads, block_size, head_dim] and dtype")
+        if a.shape[0] != src_caches[0].shape[0] or b.shape[0] != dst_caches[0].shape[0]:
+            raise ValueError("source caches must share one pool size, destination caches another")
+    _contig(block_mapping, "block_mapping")
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2 or block_mapping.dtype != torch.int64:
+        raise ValueError("block_mapping must be int64 [pairs, 2]")
+    (H, Bs, D), elt = shape
+    sp = (ctypes.c_void_p * C)(*[t.data_ptr() for t in src_caches])
+    dp = (ctypes.c_void_p * C)(*[t.data_ptr() for t in dst_caches])
+    _check(_lib.pa_swap_blocks(ctypes.cast(sp, P), ctypes.cast(dp, P), C, block_mapping.data_ptr(),
+                               int(block_mapping.shape[0]), H * Bs * D * elt, int(src_caches[0].shape[0]),
+                               int(dst_caches[0].shape[0]), _stream(stream)), "swap_blocks")
 
 
 def paged_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, cu_q_lens: torch.Tensor,

@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "pa_internal.h"
 
@@ -116,7 +117,7 @@ pa_status check_decode_common(const void *k_cache, const void *v_cache, const in
                 num_seqs, num_heads, head_dim, block_size, (long long)num_blocks, max_blocks_per_seq,
                 max_context_len);
   if (!pa::decode_supported(dtype, head_dim, block_size))
-    return fail(PA_ERR_UNSUPPORTED, "decode is built for head_dim 64/128 and block_size 4/8/16/32 (got %d, %d)",
+    return fail(PA_ERR_UNSUPPORTED, "decode is built for head_dim 64/128 and block_size 4/8/16/32/64 (got %d, %d)",
                 head_dim, block_size);
   if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs %d exceeds 65535", num_seqs);
   if (num_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "num_heads %d exceeds 65535", num_heads);
@@ -165,6 +166,26 @@ pa_status check_workspace(const DecodeGeometry &g, const void *workspace, size_t
   if (!aligned16(workspace)) return fail(PA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   return PA_OK;
 }
+
+// The address a kernel uses for p: p itself for device memory, the mapped
+// device address for pinned host memory; null for anything else (pageable
+// host memory, unknown pointers), which a kernel must never touch.
+const void *device_address(const void *p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the error the failed query left
+    return nullptr;
+  }
+  if (attr.type == hipMemoryTypeDevice) return p;
+  if (attr.type != hipMemoryTypeHost) return nullptr;
+  void *d = nullptr;
+  if (hipHostGetDevicePointer(&d, const_cast<void *>(p), 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return d;
+}
+
 
 }  // namespace
 
@@ -295,7 +316,7 @@ pa_status pa_paged_attention_decode_reduce(void *out, const int32_t *context_len
       max_context_len < 0 || split_workers < 0)
     return fail(PA_ERR_INVALID_ARG, "sizes must be positive (num_seqs, max_context_len, split_workers >= 0)");
   if (!pa::decode_supported(dtype, head_dim, block_size))
-    return fail(PA_ERR_UNSUPPORTED, "decode is built for head_dim 64/128 and block_size 4/8/16/32");
+    return fail(PA_ERR_UNSUPPORTED, "decode is built for head_dim 64/128 and block_size 4/8/16/32/64");
   if (num_seqs > 65535 || num_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs or num_heads exceeds 65535");
   if (num_seqs == 0) return ok();
   const DecodeGeometry g = geometry(head_dim, max_context_len, max_blocks_per_seq, block_size,
@@ -371,6 +392,33 @@ pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32
   a.scale_log2 = scale * kLog2e;
   return hip_status(pa::launch_prefill_chunk(a, dtype, head_dim, block_size, reinterpret_cast<hipStream_t>(stream)),
                     "prefill chunk");
+}
+
+pa_status pa_swap_blocks(const void *const *src_caches, void *const *dst_caches, int32_t num_caches,
+                         const int64_t *block_mapping, int64_t num_pairs, int64_t block_bytes,
+                         int64_t src_num_blocks, int64_t dst_num_blocks, void *stream) {
+  if (num_caches <= 0 || num_pairs < 0 || block_bytes <= 0 || src_num_blocks <= 0 || dst_num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_caches, block_bytes and both pool sizes must be positive, num_pairs >= 0");
+  if (block_bytes % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG, "block_bytes %lld is not a multiple of 16", (long long)block_bytes);
+  if (num_pairs == 0) return ok();
+  if (!src_caches || !dst_caches || !block_mapping) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  const int64_t *mapping = static_cast<const int64_t *>(device_address(block_mapping));
+  if (!mapping) return fail(PA_ERR_INVALID_ARG, "block_mapping must be device memory or pinned host memory");
+  std::vector<const void *> src(num_caches);
+  std::vector<void *> dst(num_caches);
+  for (int32_t c = 0; c < num_caches; ++c) {
+    if (!src_caches[c] || !dst_caches[c]) return fail(PA_ERR_INVALID_ARG, "cache %d: null pointer", c);
+    if (!aligned16(src_caches[c]) || !aligned16(dst_caches[c]))
+      return fail(PA_ERR_INVALID_ARG, "cache %d: caches must be 16-byte aligned", c);
+    src[c] = device_address(src_caches[c]);
+    dst[c] = const_cast<void *>(device_address(dst_caches[c]));
+    if (!src[c] || !dst[c])
+      return fail(PA_ERR_INVALID_ARG, "cache %d: caches must be device memory or pinned host memory", c);
+  }
+  return hip_status(pa::launch_swap_blocks(src.data(), dst.data(), num_caches, mapping, num_pairs, block_bytes,
+                                           src_num_blocks, dst_num_blocks, reinterpret_cast<hipStream_t>(stream)),
+                    "swap_blocks");
 }
 
 pa_status pa_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t workgroups, void *stream) {

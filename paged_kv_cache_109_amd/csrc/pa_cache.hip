@@ -128,6 +128,69 @@ hipError_t launch_copy_blocks(void *const *k_caches, void *const *v_caches, int3
   return hipSuccess;
 }
 
+// ------------------------------------------------------------- swap_blocks
+//
+// Whole-block copies from one pool to another (HBM to pinned host memory to
+// swap blocks out, or back): every (src, dst) pair of the mapping, for every
+// cache listed (e.g. the K and V caches of each layer), in one launch.  The
+// host side is reached through the host link, so loads are issued four per
+// lane at once to keep many requests in flight.
+
+struct SwapPtrs {
+  const char *src[kSwapMaxCaches];
+  char *dst[kSwapMaxCaches];
+};
+
+// grid.x = pair * chunks_per_block + chunk, grid.y = cache.
+__global__ __launch_bounds__(kCacheThreads) void swap_blocks_kernel(SwapPtrs ptrs, const int64_t *__restrict__ mapping,
+                                                                    int64_t block_bytes, int64_t src_blocks,
+                                                                    int64_t dst_blocks, int32_t chunks_per_block) {
+  const int64_t pair = blockIdx.x / chunks_per_block;
+  const int64_t chunk = blockIdx.x - pair * chunks_per_block;
+  const int64_t src = mapping[2 * pair];
+  const int64_t dst = mapping[2 * pair + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const char *from = ptrs.src[blockIdx.y] + src * block_bytes;
+  char *to = ptrs.dst[blockIdx.y] + dst * block_bytes;
+  const int64_t begin = chunk * kCopyChunk;
+  uint4 r[kCopyUnroll];
+  bool live[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t o = begin + ((int64_t)u * kCacheThreads + threadIdx.x) * 16;
+    live[u] = o < block_bytes;
+    if (live[u]) r[u] = *reinterpret_cast<const uint4 *>(from + o);
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t o = begin + ((int64_t)u * kCacheThreads + threadIdx.x) * 16;
+    if (live[u]) *reinterpret_cast<uint4 *>(to + o) = r[u];
+  }
+}
+
+hipError_t launch_swap_blocks(const void *const *src_caches, void *const *dst_caches, int32_t num_caches,
+                              const int64_t *block_mapping, int64_t num_pairs, int64_t block_bytes,
+                              int64_t src_blocks, int64_t dst_blocks, hipStream_t stream) {
+  const int64_t chunks = (block_bytes + kCopyChunk - 1) / kCopyChunk;
+  const int64_t max_pairs = 0x7fffffff / chunks;
+  for (int32_t c0 = 0; c0 < num_caches; c0 += kSwapMaxCaches) {
+    const int32_t nc = num_caches - c0 < kSwapMaxCaches ? num_caches - c0 : kSwapMaxCaches;
+    SwapPtrs p = {};
+    for (int32_t i = 0; i < nc; ++i) {
+      p.src[i] = reinterpret_cast<const char *>(src_caches[c0 + i]);
+      p.dst[i] = reinterpret_cast<char *>(dst_caches[c0 + i]);
+    }
+    for (int64_t first = 0; first < num_pairs; first += max_pairs) {
+      const int64_t np = num_pairs - first < max_pairs ? num_pairs - first : max_pairs;
+      hipLaunchKernelGGL(swap_blocks_kernel, dim3((unsigned)(np * chunks), (unsigned)nc), dim3(kCacheThreads), 0,
+                         stream, p, block_mapping + 2 * first, block_bytes, src_blocks, dst_blocks, (int32_t)chunks);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
 // ---------------------------------------------------------- streaming read
 //
 // The bandwidth reference the cache kernels are compared with on the same

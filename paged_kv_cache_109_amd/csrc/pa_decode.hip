@@ -542,6 +542,7 @@ static hipError_t launch_part(const DecodeArgs &a, hipStream_t st) {
     case 8: return FN<T, D, 8>(__VA_ARGS__);       \
     case 16: return FN<T, D, 16>(__VA_ARGS__);     \
     case 32: return FN<T, D, 32>(__VA_ARGS__);     \
+    case 64: return FN<T, D, 64>(__VA_ARGS__);     \
   }
 
 template <Dt T, int D>
@@ -577,7 +578,7 @@ static int waves_d(int D, int B) {
 bool decode_supported(int dtype, int head_dim, int block_size) {
   const bool dt = dtype >= 0 && dtype <= 2;
   const bool d = head_dim == 64 || head_dim == 128;
-  const bool b = block_size == 4 || block_size == 8 || block_size == 16 || block_size == 32;
+  const bool b = block_size == 4 || block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64;
   return dt && d && b;
 }
 

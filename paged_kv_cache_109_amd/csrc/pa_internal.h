@@ -63,6 +63,12 @@ hipError_t launch_copy_blocks(void *const *k_caches, void *const *v_caches, int3
                               const int64_t *block_mapping, int64_t num_pairs, int64_t block_bytes,
                               int64_t num_blocks, hipStream_t stream);
 
+// Most caches one swap launch covers (pointer pairs travel as kernel arguments).
+constexpr int kSwapMaxCaches = 64;
+hipError_t launch_swap_blocks(const void *const *src_caches, void *const *dst_caches, int32_t num_caches,
+                              const int64_t *block_mapping, int64_t num_pairs, int64_t block_bytes,
+                              int64_t src_blocks, int64_t dst_blocks, hipStream_t stream);
+
 // Sink words the streaming-read kernel stores per workgroup (one per wave).
 constexpr int kStreamSinkWordsPerGroup = 4;
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t workgroups,

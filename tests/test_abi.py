@@ -58,7 +58,7 @@ def decode(**over):
 
 @pytest.mark.parametrize("over,status", [
     (dict(dt=7), 1), (dict(H=0), 1), (dict(N=0), 1), (dict(M=0), 1), (dict(max_ctx=-1), 1),
-    (dict(D=96), 2), (dict(Bs=12), 2), (dict(Bs=64), 2), (dict(k=None), 1), (dict(q=FAKE + 8), 1),
+    (dict(D=96), 2), (dict(Bs=12), 2), (dict(Bs=128), 2), (dict(k=None), 1), (dict(q=FAKE + 8), 1),
     (dict(part=-1), 1), (dict(scale=float("nan")), 1),
     (dict(max_ctx=2048, M=128), 3), (dict(max_ctx=2048, M=128, ws=FAKE, ws_bytes=100), 3), (dict(S=70000), 2),
 ])
@@ -116,3 +116,14 @@ def test_stream_read_rejects_bad_arguments():
     assert f(FAKE, 0, FAKE, 8, None) == 1
     assert f(FAKE, 4096, FAKE, 0, None) == 1
     assert f(FAKE + 8, 4096, FAKE, 8, None) == 1
+
+
+def test_swap_blocks_rejects_bad_arguments():
+    f = B._lib.pa_swap_blocks
+    arr = (ctypes.c_void_p * 2)(FAKE, None)
+    p = ctypes.cast(arr, ctypes.c_void_p)
+    assert f(None, None, 1, FAKE, 3, 4096, 10, 10, None) == 1      # null cache arrays
+    assert f(p, p, 2, FAKE, 3, 4100, 10, 10, None) == 1            # block size not a multiple of 16
+    assert f(p, p, 0, FAKE, 3, 4096, 10, 10, None) == 1            # no caches
+    assert f(p, p, 2, FAKE, 3, 4096, 0, 10, None) == 1             # empty source pool
+    assert f(None, None, 1, None, 0, 4096, 10, 10, None) == 0      # no pairs: no-op

@@ -145,3 +145,47 @@ def test_stream_read_reads_every_word(words16, groups):
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(data)
+
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_swap_blocks_out_to_pinned_host_and_back_bit_exact(dtype):
+    """Blocks of every layer's K and V go from the device pool to a pinned
+    host pool and back to other device blocks; both whole pools must equal
+    the oracle's byte for byte (so nothing else was written)."""
+    rng = np.random.default_rng(31)
+    Nd, Nh, L, H, B, D = 40, 12, 2, 3, 16, 64
+    dev_np = [W.cast(rng.standard_normal((Nd, H, B, D), dtype=np.float32), dtype) for _ in range(2 * L)]
+    host_np = [W.cast(rng.standard_normal((Nh, H, B, D), dtype=np.float32), dtype) for _ in range(2 * L)]
+    dev_t = [dev(a, dtype) for a in dev_np]
+    def pinned(a):
+        t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if dtype == "bf16" else a))
+        return (t.view(torch.bfloat16) if dtype == "bf16" else t).pin_memory()
+
+    host_t = [pinned(a) for a in host_np]
+    assert all(t.is_pinned() for t in host_t)
+    out_map = np.stack([rng.choice(Nd, 9, replace=False), rng.choice(Nh, 9, replace=False)], axis=1)
+    say(f"  swap out {dtype}: {len(out_map)} blocks x {2 * L} caches to pinned host memory")
+    pa.swap_blocks(dev_t, host_t, dev(out_map.astype(np.int64)))
+    torch.cuda.synchronize()
+    oracle.swap_blocks(dev_np, host_np, out_map)
+    for t, a in zip(host_t, host_np):
+        assert host(t, dtype).tobytes() == a.tobytes()
+    in_map = np.stack([out_map[:, 1], rng.choice(Nd, 9, replace=False)], axis=1).astype(np.int64)
+    in_map_pinned = torch.from_numpy(in_map).pin_memory()
+    say(f"  swap in {dtype}: mapping in pinned host memory")
+    pa.swap_blocks(host_t, dev_t, in_map_pinned)
+    torch.cuda.synchronize()
+    oracle.swap_blocks(host_np, dev_np, in_map)
+    for t, a in zip(dev_t, dev_np):
+        assert host(t, dtype).tobytes() == a.tobytes()
+
+
+def test_swap_blocks_refuses_pageable_host_memory():
+    # The mapping's source index is outside the pool, so even a launch
+    # would touch no cache block; the call must refuse before launching.
+    src = torch.zeros(4, 2, 16, 64, dtype=torch.float16)  # ordinary (pageable) host memory
+    dst = torch.zeros(4, 2, 16, 64, dtype=torch.float16, device="cuda")
+    mapping = torch.tensor([[1 << 40, 0]], dtype=torch.int64, device="cuda")
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.swap_blocks([src], [dst], mapping)
+    assert e.value.status == 1 and "pinned" in str(e.value)

@@ -45,7 +45,7 @@ LENS = [1, 3, 15, 16, 17, 31, 64, 100, 511, 512, 513, 700, 1030]
 
 @pytest.mark.parametrize("dtype", W.DTYPES)
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("B", [4, 8, 16, 32])
+@pytest.mark.parametrize("B", [4, 8, 16, 32, 64])
 def test_decode_shapes(dtype, D, B):
     c = W.make_decode_case(len(LENS), 3, D, B, dtype, LENS, seed=B * D, extra_blocks=5,
                            max_blocks_per_seq=W.blocks_needed(max(LENS), B) + 2, poison_unused=True, pad_entry=-1)

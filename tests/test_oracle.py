@@ -337,3 +337,24 @@ def test_copy_on_write_walkthrough():
         V = np.concatenate([f64(pv, dtype), f64(new, dtype)], axis=0).transpose(1, 0, 2)
         want = sdpa(f64(q[s], dtype)[:, None, :], K, V, D ** -0.5)[:, 0, :]
         np.testing.assert_allclose(out[s], want, rtol=1e-12, atol=1e-13)
+
+
+def test_swap_blocks_round_trip_restores_the_pool():
+    """Swapping blocks out to a second pool and back to their own places
+    leaves the first pool as it was; blocks outside the mapping never
+    change, and the second pool holds exactly the swapped blocks."""
+    rng = np.random.default_rng(4)
+    gpu = [rng.integers(0, 255, size=(9, 2, 4, 16), dtype=np.uint8) for _ in range(2)]
+    host = [np.zeros((5, 2, 4, 16), np.uint8) for _ in range(2)]
+    keep = [g.copy() for g in gpu]
+    out = np.array([[7, 0], [2, 3], [4, 1]])
+    oracle.swap_blocks(gpu, host, out)
+    for g, h in zip(gpu, host):
+        assert np.array_equal(h[[0, 3, 1]], g[[7, 2, 4]]) and not h[[2, 4]].any()
+    for g in gpu:
+        g[[7, 2, 4]] = 0
+    oracle.swap_blocks(host, gpu, out[:, ::-1])
+    for g, k in zip(gpu, keep):
+        assert np.array_equal(g, k)
+    with pytest.raises(oracle.OracleError):
+        oracle.swap_blocks(gpu, host, [[0, 1], [2, 1]])

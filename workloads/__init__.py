@@ -301,25 +301,36 @@ def tiny_f32(seed: int = 0, poisoned: bool = False) -> PagedCase:
         name="tiny_f32" + ("_poisoned" if poisoned else ""))
 
 
-def opt13b_b64(seed: int = 0, dtype: str = "f16") -> PagedCase:
-    """OPT-13B layer: batch 64, 40 heads x 128, B=16, lengths uniform in
-    [1, 2048]; the pool holds exactly the needed blocks, placed by a random
-    permutation; one new token per sequence at position ctx-1."""
+def _shape(block_size: int) -> dict:
+    return dict(OPT13B, block_size=block_size)
+
+
+def _suffix(block_size: int) -> str:
+    return "" if block_size == OPT13B["block_size"] else f"_B{block_size}"
+
+
+def opt13b_b64(seed: int = 0, dtype: str = "f16", block_size: int = 16) -> PagedCase:
+    """OPT-13B layer: batch 64, 40 heads x 128, B=16 (or block_size),
+    lengths uniform in [1, 2048]; the pool holds exactly the needed blocks,
+    placed by a random permutation; one new token per sequence at position
+    ctx-1."""
     return make_decode_case(
         64, dtype=dtype, context_lens=lambda r, n: r.integers(1, 2049, size=n), seed=seed,
-        max_blocks_per_seq=128, new_tokens=True, name="opt13b_b64_" + dtype, **OPT13B)
+        max_blocks_per_seq=-(-2048 // block_size), new_tokens=True,
+        name="opt13b_b64_" + dtype + _suffix(block_size), **_shape(block_size))
 
 
 def _lognormal_ctx(r, n):
     return np.clip(np.rint(r.lognormal(mean=np.log(300.0), sigma=1.0, size=n)), 8, 2048).astype(np.int32)
 
 
-def large_batch_b256(seed: int = 0, dtype: str = "f16") -> PagedCase:
+def large_batch_b256(seed: int = 0, dtype: str = "f16", block_size: int = 16) -> PagedCase:
     """Batch 256 with lognormal lengths (median 300, sigma 1, clipped to
     [8, 2048]), random placement; one new token per sequence at ctx-1."""
     return make_decode_case(
         256, dtype=dtype, context_lens=_lognormal_ctx, seed=seed,
-        max_blocks_per_seq=128, new_tokens=True, name="large_batch_b256_" + dtype, **OPT13B)
+        max_blocks_per_seq=-(-2048 // block_size), new_tokens=True,
+        name="large_batch_b256_" + dtype + _suffix(block_size), **_shape(block_size))
 
 
 def parallel_sampling(seed: int = 0, prompt_len: int = 512, groups: int = 32, samples: int = 6,
@@ -358,7 +369,7 @@ def parallel_sampling(seed: int = 0, prompt_len: int = 512, groups: int = 32, sa
     q = normal_cast(rng, (S, num_heads, head_dim), dtype)
     k, v = _fill_pool(rng, N, num_heads, B, head_dim, dtype)
     return PagedCase(
-        name=f"parallel_sampling_p{prompt_len}_{dtype}", dtype=dtype, num_heads=num_heads,
+        name=f"parallel_sampling_p{prompt_len}_{dtype}" + _suffix(B), dtype=dtype, num_heads=num_heads,
         head_dim=head_dim, block_size=B, context_lens=ctx, block_tables=_tables(seq_blocks, M, 0),
         q=q, k_cache=k, v_cache=v, scale=1.0 / float(np.sqrt(head_dim)), seq_blocks=seq_blocks,
         block_mapping=np.asarray(pairs, dtype=np.int64).reshape(-1, 2))
