@@ -183,6 +183,51 @@ pa_status pa_paged_attention_decode_reduce(void *out, const int32_t *context_len
                                            size_t workspace_bytes, void *stream);
 
 /*
+ * pa_paged_attention_decode_shared -- decode for groups of sequences that
+ * share a prompt (parallel sampling), reading the shared blocks once per
+ * group instead of once per sequence.  Same result as
+ * pa_paged_attention_decode, up to floating-point summation order.
+ *
+ * Samples forked from one prompt point their block tables at the same
+ * physical blocks for it (paper notes "PagedAttention: Efficient Memory
+ * Management for Large Language Model Serving", section 3.4.1 Parallel
+ * sampling; "KV 캐시 관리와 PagedAttention", section on sharing the common KV
+ * of several responses).  Attention splits by position range (review
+ * section 4.1), so the call computes, per (sequence, head): the shared
+ * prefix [0, P) for all members of a group at once, each member's own
+ * positions [P, n) with the stream-K pass, and their merge.
+ *
+ *  group_members  device int32 [num_groups][PA_MAX_GROUP_MEMBERS]: the
+ *                 members of each group, a leading run of sequence ids,
+ *                 padded with -1.  A sequence is in at most one group.
+ *  group_prefix   device int32 [num_groups]: P, the tokens whose blocks all
+ *                 members share (same physical block ids at the same table
+ *                 entries), a multiple of 16 and of block_size, at most
+ *                 every member's context length.
+ *  seq_starts     device int32 [num_seqs]: P of the sequence's group, 0 for
+ *                 a sequence in no group (decoded as usual).
+ *  max_prefix_len host upper bound of group_prefix.
+ *  workspace      >= pa_decode_shared_workspace_bytes(...) bytes, 16-byte
+ *                 aligned; needs no initialisation.
+ * Other arguments as for pa_paged_attention_decode.  block_size 16, 32 or
+ * 64 (PA_ERR_UNSUPPORTED otherwise).  The group description is not checked
+ * against the tables on the host (that needs device data); an inconsistent
+ * one gives wrong results, never an access outside the given arrays.
+ */
+#define PA_MAX_GROUP_MEMBERS 8
+size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                        int32_t max_context_len, int32_t block_size,
+                                        int32_t num_groups, int32_t max_prefix_len,
+                                        int32_t split_workers);
+pa_status pa_paged_attention_decode_shared(
+    void *out, const void *q, const void *k_cache, const void *v_cache, const int32_t *block_tables,
+    int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+    int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+    float scale, pa_dtype dtype, const int32_t *group_members, const int32_t *group_prefix,
+    const int32_t *seq_starts, int32_t num_groups, int32_t max_prefix_len, int32_t split_workers,
+    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * pa_copy_blocks -- batched whole-block copy for copy-on-write.
  *
  * The fused block-copy kernel (review section 5.1, item 3; notes section

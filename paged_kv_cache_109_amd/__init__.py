@@ -13,6 +13,8 @@ from ._binding import (  # noqa: F401
     STREAM_SINK_WORDS_PER_GROUP,
     PagedAttnError,
     abi_version,
+    MAX_GROUP_MEMBERS,
+    alloc_decode_shared_workspace,
     alloc_decode_workspace,
     copy_blocks,
     decode_default_workers,
@@ -20,9 +22,11 @@ from ._binding import (  # noqa: F401
     paged_attention_decode,
     paged_attention_decode_partitions,
     paged_attention_decode_reduce,
+    paged_attention_decode_shared,
     paged_attention_prefill_chunk,
     reshape_and_cache,
     stream_read,
     swap_blocks,
 )
+from .sharing import shared_prefix_groups  # noqa: F401
 from .slots import slot_mapping  # noqa: F401

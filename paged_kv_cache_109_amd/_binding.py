@@ -44,6 +44,10 @@ _SIGS = {
         [P, P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, P], ctypes.c_int),
     "pa_stream_read": ([P, i64, P, i32, P], ctypes.c_int),
     "pa_swap_blocks": ([P, P, i32, P, i64, i64, i64, i64, P], ctypes.c_int),
+    "pa_decode_shared_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32, i32], sz),
+    "pa_paged_attention_decode_shared": (
+        [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, P, P, P, i32, i32, i32, P, sz, P],
+        ctypes.c_int),
     "pa_bm_create": ([i64, i32, i32, P, P], ctypes.c_int),
     "pa_bm_destroy": ([P], None),
     "pa_bm_num_free": ([P], i64),
@@ -181,6 +185,50 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
     _check(_lib.pa_paged_attention_decode(*_decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
                                                         max_context_len, scale, split_workers, workspace,
                                                         stream)), "paged_attention_decode")
+    return out
+
+
+MAX_GROUP_MEMBERS = 8
+
+
+def alloc_decode_shared_workspace(num_seqs, num_heads, head_dim, max_context_len, block_size, num_groups,
+                                  max_prefix_len, split_workers=0, device="cuda") -> Optional[torch.Tensor]:
+    n = int(_lib.pa_decode_shared_workspace_bytes(int(num_seqs), int(num_heads), int(head_dim),
+                                                  int(max_context_len), int(block_size), int(num_groups),
+                                                  int(max_prefix_len), int(split_workers)))
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def paged_attention_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                  block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                                  scale: float, group_members: torch.Tensor, group_prefix: torch.Tensor,
+                                  seq_starts: torch.Tensor, max_prefix_len: int,
+                                  workspace: Optional[torch.Tensor] = None, split_workers: int = 0,
+                                  stream=None) -> torch.Tensor:
+    """Decode where groups of sequences share the blocks of a prompt prefix:
+    group_members int32 [G, 8] (sequence ids, -1 padded), group_prefix int32
+    [G] (shared tokens), seq_starts int32 [S] (the prefix of a sequence's
+    group, else 0), all device tensors -- see sharing.shared_prefix_groups.
+    Same result as paged_attention_decode; each shared block is read once
+    per group."""
+    G = int(group_members.shape[0])
+    if group_members.dim() != 2 or group_members.shape[1] != MAX_GROUP_MEMBERS or group_prefix.shape != (G,):
+        raise ValueError(f"group_members must be [groups, {MAX_GROUP_MEMBERS}] and group_prefix [groups]")
+    if seq_starts.shape != (q.shape[0],):
+        raise ValueError("seq_starts must be [num_seqs]")
+    for t, n in ((group_members, "group_members"), (group_prefix, "group_prefix"), (seq_starts, "seq_starts")):
+        _contig(t, n)
+    if workspace is None:
+        workspace = alloc_decode_shared_workspace(q.shape[0], k_cache.shape[1], k_cache.shape[3], max_context_len,
+                                                  k_cache.shape[2], G, max_prefix_len, split_workers,
+                                                  device=q.device)
+    args = list(_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                             split_workers, workspace, stream))
+    ws_ptr, ws_bytes, st = args[-3:]
+    _check(_lib.pa_paged_attention_decode_shared(
+        *args[:15], _dev(group_members, "group_members", torch.int32), _dev(group_prefix, "group_prefix", torch.int32),
+        _dev(seq_starts, "seq_starts", torch.int32), G, int(max_prefix_len), int(split_workers), ws_ptr, ws_bytes,
+        st), "paged_attention_decode_shared")
     return out
 
 

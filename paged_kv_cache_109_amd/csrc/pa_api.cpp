@@ -154,6 +154,9 @@ pa::DecodeArgs decode_args(void *out, const void *q, const void *k_cache, const 
   a.workers = (int32_t)g.workers;
   a.out_row_words = (int32_t)((int64_t)num_heads * head_dim * elt_bytes(dtype) / 4);
   a.scale_log2 = scale * kLog2e;
+  a.starts = nullptr;
+  a.suffix_out = nullptr;
+  a.suffix_row = num_heads * (head_dim + 2);
   return a;
 }
 
@@ -186,6 +189,27 @@ const void *device_address(const void *p) {
   return d;
 }
 
+
+struct SharedGeometry {
+  DecodeGeometry dec;
+  int32_t chunks;
+  size_t suffix_off, partials_off, ws_bytes;
+};
+
+SharedGeometry shared_geometry(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
+                               int32_t max_blocks, int32_t block_size, int64_t workers, int32_t num_groups,
+                               int32_t max_prefix_len) {
+  SharedGeometry g;
+  g.dec = geometry(head_dim, max_context_len, max_blocks, block_size, workers);
+  const int64_t prefix_tiles = ceil_div(std::max<int32_t>(max_prefix_len, 0), pa::kDecodeTile);
+  g.chunks = (int32_t)std::max<int64_t>(1, ceil_div(prefix_tiles, pa::kPrefixChunkTiles));
+  const size_t row = (size_t)head_dim + 2;
+  g.suffix_off = round_up(g.dec.ws_bytes, 256);
+  g.partials_off = round_up(g.suffix_off + (size_t)num_seqs * num_heads * row * sizeof(float), 256);
+  g.ws_bytes = g.partials_off +
+               (size_t)num_groups * g.chunks * num_heads * pa::kSharedMaxMembers * row * sizeof(float);
+  return g;
+}
 
 }  // namespace
 
@@ -329,6 +353,81 @@ pa_status pa_paged_attention_decode_reduce(void *out, const int32_t *context_len
                                        num_seqs, num_heads, head_dim, dtype, 1, 1.f, g, workspace);
   return hip_status(pa::launch_decode_reduce(a, dtype, head_dim, reinterpret_cast<hipStream_t>(stream)),
                     "decode reduce");
+}
+
+size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                        int32_t max_context_len, int32_t block_size, int32_t num_groups,
+                                        int32_t max_prefix_len, int32_t split_workers) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_context_len < 0 ||
+      num_groups < 0 || max_prefix_len < 0 || split_workers < 0)
+    return 0;
+  return shared_geometry(num_seqs, num_heads, head_dim, max_context_len, -1, block_size,
+                         worker_bound(split_workers), num_groups, max_prefix_len)
+      .ws_bytes;
+}
+
+pa_status pa_paged_attention_decode_shared(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                           const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                                           int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                           int64_t num_blocks, float scale, pa_dtype dtype,
+                                           const int32_t *group_members, const int32_t *group_prefix,
+                                           const int32_t *seq_starts, int32_t num_groups, int32_t max_prefix_len,
+                                           int32_t split_workers, void *workspace, size_t workspace_bytes,
+                                           void *stream) {
+  pa_status st = check_decode_common(k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                                     max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks,
+                                     dtype, split_workers);
+  if (st != PA_OK) return st;
+  if (!pa::shared_supported(dtype, head_dim, block_size))
+    return fail(PA_ERR_UNSUPPORTED, "shared-prefix decode is built for block_size 16/32/64 (got %d)", block_size);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  if (num_groups < 0 || max_prefix_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "num_groups and max_prefix_len must be >= 0");
+  if (num_seqs > 0 && (!out || !q || !seq_starts)) return fail(PA_ERR_INVALID_ARG, "null out, q or seq_starts");
+  if (num_groups > 0 && (!group_members || !group_prefix))
+    return fail(PA_ERR_INVALID_ARG, "null group_members or group_prefix");
+  if (!aligned16(out) || !aligned16(q)) return fail(PA_ERR_INVALID_ARG, "out and q must be 16-byte aligned");
+  if (num_seqs == 0) return ok();
+  const int64_t workers = decode_workers(dtype, head_dim, block_size, split_workers);
+  const SharedGeometry g = shared_geometry(num_seqs, num_heads, head_dim, max_context_len, max_blocks_per_seq,
+                                           block_size, workers, num_groups, max_prefix_len);
+  if (!workspace || workspace_bytes < g.ws_bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", g.ws_bytes, workspace_bytes);
+  if (!aligned16(workspace)) return fail(PA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  char *ws = reinterpret_cast<char *>(workspace);
+  pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                 num_heads, head_dim, dtype, num_blocks, scale, g.dec, workspace);
+  a.starts = seq_starts;
+  a.suffix_out = reinterpret_cast<float *>(ws + g.suffix_off);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = hip_status(pa::launch_decode_partitions(a, dtype, head_dim, block_size, s), "decode partitions");
+  if (st != PA_OK) return st;
+  st = hip_status(pa::launch_decode_reduce(a, dtype, head_dim, s), "decode reduce");
+  if (st != PA_OK) return st;
+  pa::SharedArgs sa;
+  sa.out = out;
+  sa.q = q;
+  sa.k_cache = k_cache;
+  sa.v_cache = v_cache;
+  sa.block_tables = block_tables;
+  sa.context_lens = context_lens;
+  sa.starts = seq_starts;
+  sa.members = group_members;
+  sa.prefix = group_prefix;
+  sa.partials = reinterpret_cast<float *>(ws + g.partials_off);
+  sa.suffix = a.suffix_out;
+  sa.num_blocks = num_blocks;
+  sa.num_seqs = num_seqs;
+  sa.num_heads = num_heads;
+  sa.max_blocks = max_blocks_per_seq;
+  sa.num_groups = num_groups;
+  sa.chunks = g.chunks;
+  sa.chunk_tiles = pa::kPrefixChunkTiles;
+  sa.ctx_cap = g.dec.ctx_cap;
+  sa.suffix_row = a.suffix_row;
+  sa.scale_log2 = a.scale_log2;
+  return hip_status(pa::launch_shared_prefix_and_combine(sa, dtype, head_dim, block_size, s), "shared prefix");
 }
 
 pa_status pa_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t num_layers,

@@ -82,6 +82,35 @@ struct RowShape {
 __device__ __forceinline__ int clip_ctx(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
 __device__ __forceinline__ int tiles_of(int n) { return (n + kDecodeTile - 1) / kDecodeTile; }
 
+// First position the pass covers for a sequence of n (clipped) tokens: 0,
+// or with a shared prefix its start, rounded down to a whole tile and
+// clamped to [0, n].
+__device__ __forceinline__ int start_of(int raw_start, int n) {
+  const int st = raw_start < 0 ? 0 : (raw_start & ~(kDecodeTile - 1));
+  return st < n ? st : n;
+}
+// Tiles of sequence s (n clipped tokens) the pass covers.
+__device__ __forceinline__ int pass_tiles(const DecodeArgs &a, int s, int n) {
+  return a.starts ? tiles_of(n - start_of(a.starts[s], n)) : tiles_of(n);
+}
+// Whether the pass leaves partials (not the output) for sequence s.
+__device__ __forceinline__ bool to_partial(const DecodeArgs &a, int start) { return a.suffix_out && start > 0; }
+
+// The result of a sequence with no tile in the pass: a zero output row, or
+// with a shared prefix an empty partial (zero sum, log2-denominator -inf)
+// for every head.  Written by `count` cooperating lanes from `first`.
+__device__ __forceinline__ void empty_rows(const DecodeArgs &a, int s, int first, int count) {
+  const int n = clip_ctx(a.context_lens[s], a.ctx_cap);
+  if (a.starts && to_partial(a, start_of(a.starts[s], n))) {
+    float *row = a.suffix_out + (int64_t)s * a.suffix_row;
+    const int per_head = a.suffix_row / a.num_heads;  // head_dim + 2
+    for (int i = first; i < a.suffix_row; i += count) row[i] = (i % per_head == per_head - 2) ? -INFINITY : 0.f;
+  } else {
+    uint32_t *row = reinterpret_cast<uint32_t *>(a.out) + (int64_t)s * a.out_row_words;
+    for (int i = first; i < a.out_row_words; i += count) row[i] = 0u;  // +0.0 in every dtype
+  }
+}
+
 // Range [g0, g1) of global tiles owned by worker wave w of G.
 __device__ __forceinline__ uint32_t range_begin(uint32_t w, uint32_t total, uint32_t G) {
   return (uint32_t)(((uint64_t)w * total) / G);
@@ -113,7 +142,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
   const int per = (S + kPlanThreads - 1) / kPlanThreads;
   const int lo = min(S, tid * per), hi = min(S, lo + per);
   uint32_t mine = 0;
-  for (int s = lo; s < hi; ++s) mine += (uint32_t)tiles_of(clip_ctx(a.context_lens[s], a.ctx_cap)) * H;
+  for (int s = lo; s < hi; ++s) mine += (uint32_t)pass_tiles(a, s, clip_ctx(a.context_lens[s], a.ctx_cap)) * H;
   scan[tid] = mine;
   __syncthreads();
   for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive Hillis-Steele scan
@@ -132,7 +161,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
   }
   for (int s = lo; s < hi; ++s) {
     const int n = clip_ctx(a.context_lens[s], a.ctx_cap);
-    const uint32_t ts = (uint32_t)tiles_of(n);
+    const uint32_t ts = (uint32_t)pass_tiles(a, s, n);
     const uint32_t c_next = c + ts * H;
     if (ts > 0) {
       // Workers whose first tile falls in [c, c_next): w in [ceil(c*G/T), ceil(c_next*G/T)).
@@ -144,8 +173,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
         a.plan[kPlanHeader + 2 * w + 1] = local % ts;
       }
     } else {
-      uint32_t *row = reinterpret_cast<uint32_t *>(a.out) + (int64_t)s * a.out_row_words;
-      for (int i = 0; i < a.out_row_words; ++i) row[i] = 0u;  // +0.0 in every dtype
+      empty_rows(a, s, 0, 1);
     }
     c = c_next;
   }
@@ -157,8 +185,16 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
 struct Cursor {
   int s, h, t;     // sequence, head, tile within the pair
   int n, nt;       // context length and tiles of sequence s
+  int st;          // first position of sequence s in the pass (0 without a shared prefix)
   uint32_t g;      // global tile index
 };
+
+// Length, start and tiles of the sequence under the cursor.
+__device__ __forceinline__ void cursor_load(Cursor &c, const DecodeArgs &a) {
+  c.n = clip_ctx(load_uniform(a.context_lens, c.s), a.ctx_cap);
+  c.st = a.starts ? start_of(load_uniform(a.starts, c.s), c.n) : 0;
+  c.nt = tiles_of(c.n - c.st);
+}
 
 // Step to the next tile; crosses to the next head, then to the next
 // non-empty sequence.  Only called while g + 1 < end, so a next tile exists.
@@ -170,8 +206,7 @@ __device__ __forceinline__ void cursor_next(Cursor &c, const DecodeArgs &a) {
   c.h = 0;
   do {
     ++c.s;
-    c.n = clip_ctx(load_uniform(a.context_lens, c.s), a.ctx_cap);
-    c.nt = tiles_of(c.n);
+    cursor_load(c, a);
   } while (c.nt == 0);
 }
 
@@ -203,15 +238,22 @@ __device__ __forceinline__ bool self_plan(const DecodeArgs &a, uint32_t w, uint3
   const int S = a.num_seqs;
   const int k = (S + kWave - 1) / kWave;  // wave-uniform, 1 .. kMaxPerLane
   const int first = lane * k;
-  int32_t raw[kMaxPerLane];
+  int32_t raw[kMaxPerLane], raw_st[kMaxPerLane];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i)
+  for (int i = 0; i < kMaxPerLane; ++i) {
     if (i < k) raw[i] = a.context_lens[min(first + i, S - 1)];
+    if (i < k) raw_st[i] = a.starts ? a.starts[min(first + i, S - 1)] : 0;
+  }
   uint32_t tiles[kMaxPerLane];
   uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) {
-    tiles[i] = (i < k && first + i < S) ? (uint32_t)tiles_of(clip_ctx(raw[i], a.ctx_cap)) : 0u;
+    if (i < k && first + i < S) {
+      const int n = clip_ctx(raw[i], a.ctx_cap);
+      tiles[i] = (uint32_t)tiles_of(n - start_of(raw_st[i], n));
+    } else {
+      tiles[i] = 0u;
+    }
     mine += tiles[i] * H;
   }
   const uint32_t incl = wave_inclusive_scan(mine);
@@ -224,17 +266,13 @@ __device__ __forceinline__ bool self_plan(const DecodeArgs &a, uint32_t w, uint3
   // Zero the rows of empty sequences, each row by one whole wave.
   const uint32_t zero_waves = G > 0 ? G : 1u;
   if (w < zero_waves) {
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      if (i >= k) break;
+    for (int i = 0; i < k; ++i) {
       const int s = first + i;
       uint64_t todo = __builtin_amdgcn_ballot_w64(s < S && tiles[i] == 0 && (uint32_t)s % zero_waves == w);
       while (todo) {
         const int l = __builtin_ctzll(todo);
         todo &= todo - 1;
-        uint4 *row = reinterpret_cast<uint4 *>(reinterpret_cast<uint32_t *>(a.out) +
-                                               (int64_t)(l * k + i) * a.out_row_words);
-        for (int j = lane; j < a.out_row_words / 4; j += kWave) row[j] = make_uint4(0, 0, 0, 0);
+        empty_rows(a, l * k + i, lane, kWave);
       }
     }
   }
@@ -283,11 +321,20 @@ __device__ __forceinline__ void merge_fragments(const DecodeArgs &a, uint32_t wa
   float L = 0.f;
   for (uint32_t v = wa; v <= wb; ++v) L += frag(v)[D + 1] * fast_exp2(frag(v)[D] - mu);
   const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int n = clip_ctx(a.context_lens[s], a.ctx_cap);
+  float *part = nullptr;
+  if (a.starts && to_partial(a, start_of(a.starts[s], n)))
+    part = a.suffix_out + (int64_t)s * a.suffix_row + (int64_t)h * (D + 2);
   const int64_t out_row = ((int64_t)s * a.num_heads + h) * D;
   for (int d = lane; d < D; d += kWave) {
     float A = 0.f;
     for (uint32_t v = wa; v <= wb; ++v) A += frag(v)[d] * fast_exp2(frag(v)[D] - mu);
-    store_out_elem<T, D>(a.out, out_row + d, A * inv);
+    if (part) part[d] = A * inv;
+    else store_out_elem<T, D>(a.out, out_row + d, A * inv);
+  }
+  if (part && lane == 0) {
+    part[D] = L > 0.f ? mu + __builtin_amdgcn_logf(L) : -INFINITY;
+    part[D + 1] = 0.f;
   }
 }
 
@@ -317,8 +364,7 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_
   const char *vbase = reinterpret_cast<const char *>(a.v_cache);
   const int64_t block_stride = (int64_t)a.num_heads * B * R::kRowBytes;
 
-  ic.n = clip_ctx(load_uniform(a.context_lens, ic.s), a.ctx_cap);
-  ic.nt = tiles_of(ic.n);
+  cursor_load(ic, a);
   ic.g = g0;
   Cursor cc = ic;  // consume cursor
 
@@ -338,7 +384,7 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_
     const int s = live ? ic.s : 0, h = live ? ic.h : 0;
     const char *qp = reinterpret_cast<const char *>(a.q) + ((int64_t)s * a.num_heads + h) * R::kRowBytes;
     qf = *reinterpret_cast<const uint4 *>(qp + col * 16);
-    const int base = ic.t * kDecodeTile;
+    const int base = ic.st + ic.t * kDecodeTile;
     const int64_t head_off = (int64_t)ic.h * B * R::kRowBytes + col * 16;
     // A table entry is read only for a block whose first token is < n, so the
     // read stays inside the sequence's row.  With B >= 16 one entry covers
@@ -393,8 +439,18 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_
     const uint32_t pair_start = cc.g - (uint32_t)cc.t;
     const uint32_t pair_end = pair_start + (uint32_t)cc.nt;
     if (pair_start >= g0 && pair_end <= g1) {
-      if (lane < R::kLPT) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+      if (to_partial(a, cc.st)) {
+        float *f = a.suffix_out + (int64_t)cc.s * a.suffix_row + (int64_t)cc.h * (D + 2);
+        if (lane < R::kLPT) {
+#pragma unroll
+          for (int e = 0; e < R::kFE; ++e) f[col * R::kFE + e] = acc[e] * inv;
+        }
+        if (lane == 0) {
+          f[D] = l_run > 0.f ? m_run + __builtin_amdgcn_logf(l_run) : -INFINITY;
+          f[D + 1] = 0.f;
+        }
+      } else if (lane < R::kLPT) {
         float o[R::kFE];
 #pragma unroll
         for (int e = 0; e < R::kFE; ++e) o[e] = acc[e] * inv;
@@ -502,7 +558,7 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_reduce_ker
   const int s = (int)(sh & 0xffffu), h = (int)(sh >> 16);
   const uint32_t t = a.plan[kPlanHeader + 2 * w + 1];
   if (t == 0) return;  // the pair starts at g0: not cut at the front of this range
-  const uint32_t nt = (uint32_t)tiles_of(clip_ctx(a.context_lens[s], a.ctx_cap));
+  const uint32_t nt = (uint32_t)pass_tiles(a, s, clip_ctx(a.context_lens[s], a.ctx_cap));
   const uint32_t pair_start = g0 - t;
   if (pair_start + nt > g1) return;  // continues past this range: a later worker merges it
   merge_fragments<T, D>(a, first_worker(pair_start, total, G), w, s, h);

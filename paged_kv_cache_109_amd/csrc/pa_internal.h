@@ -33,6 +33,14 @@ struct DecodeArgs {
   int32_t workers;        // worker waves launched (the split of the tile stream)
   int32_t out_row_words;  // 32-bit words of one sequence's output rows (H*D*elt/4)
   float scale_log2;       // softmax scale * log2(e)
+  // Shared-prefix decode only (both null otherwise): starts[s] is the first
+  // position the pass covers for sequence s (a multiple of kDecodeTile);
+  // for s with starts[s] > 0 the pass leaves fp32 partials in suffix_out
+  // ([S][H][D + 2]: the normalised output, then log2 of its softmax
+  // denominator in the scale*log2(e) domain) instead of writing out.
+  const int32_t *starts;
+  float *suffix_out;
+  int32_t suffix_row;  // floats of suffix_out per sequence: num_heads * (head_dim + 2)
 };
 
 // 32-bit words before the per-worker starts in the plan.
@@ -91,6 +99,40 @@ struct PrefillArgs {
   int32_t ctx_cap;
   float scale_log2;
 };
+
+// Shared-prefix decode (pa_shared.hip): members per group, prefix tiles per
+// work item of the prefix kernel.
+constexpr int kSharedMaxMembers = 8;
+static_assert(kSharedMaxMembers == PA_MAX_GROUP_MEMBERS, "group width of the C ABI");
+constexpr int kPrefixChunkTiles = 8;
+
+struct SharedArgs {
+  void *out;                    // [S][H][D]
+  const void *q;                // [S][H][D]
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_tables;  // [S][max_blocks]
+  const int32_t *context_lens;  // [S]
+  const int32_t *starts;        // [S] first position of each sequence's own part (0: not in a group)
+  const int32_t *members;       // [G][kSharedMaxMembers] sequence ids, -1 past the last member
+  const int32_t *prefix;        // [G] shared prefix tokens
+  float *partials;              // [G][chunks][H][kSharedMaxMembers][D + 2]: value sums, max, sum
+  const float *suffix;          // [S][H][D + 2]: the decode pass's partials of the own parts
+  int64_t num_blocks;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t max_blocks;
+  int32_t num_groups;
+  int32_t chunks;               // prefix chunks per group
+  int32_t chunk_tiles;          // tiles per chunk
+  int32_t ctx_cap;
+  int32_t suffix_row;           // H * (D + 2)
+  float scale_log2;
+};
+
+bool shared_supported(int dtype, int head_dim, int block_size);
+hipError_t launch_shared_prefix_and_combine(const SharedArgs &a, int dtype, int head_dim, int block_size,
+                                            hipStream_t stream);
 
 bool prefill_supported(int dtype, int head_dim, int block_size);
 hipError_t launch_prefill_chunk(const PrefillArgs &a, int dtype, int head_dim, int block_size,

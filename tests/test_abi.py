@@ -127,3 +127,21 @@ def test_swap_blocks_rejects_bad_arguments():
     assert f(p, p, 0, FAKE, 3, 4096, 10, 10, None) == 1            # no caches
     assert f(p, p, 2, FAKE, 3, 4096, 0, 10, None) == 1             # empty source pool
     assert f(None, None, 1, None, 0, 4096, 10, 10, None) == 0      # no pairs: no-op
+
+
+def test_shared_decode_rejects_bad_arguments():
+    f = B._lib.pa_paged_attention_decode_shared
+
+    def call(**over):
+        a = dict(Bs=16, members=FAKE, prefix=FAKE, starts=FAKE, G=1, maxp=32, ws=None, ws_bytes=0)
+        a.update(over)
+        return f(FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 100, 2, 4, 128, a["Bs"], 64, 0.1, 1, a["members"],
+                 a["prefix"], a["starts"], a["G"], a["maxp"], 0, a["ws"], a["ws_bytes"], None)
+    assert call(Bs=8) == 2              # blocks of 8 are not built for the shared path
+    assert call(members=None) == 1      # groups without members
+    assert call(starts=None) == 1
+    assert call(G=-1) == 1
+    assert call() == 3                  # workspace missing
+    n = B._lib.pa_decode_shared_workspace_bytes
+    assert n(2, 4, 128, 100, 16, 1, 32, 7) > B._lib.pa_decode_workspace_bytes(2, 4, 128, 100, 16, 7)
+    assert n(0, 4, 128, 100, 16, 1, 32, 7) == 0
