@@ -322,6 +322,42 @@ def main():
         print(f"[bench] swap_blocks {P} blocks x 2 caches: to host {swap_bytes / sw['out'] / 1e9:.1f} GB/s, "
               f"from host {swap_bytes / sw['in'] / 1e9:.1f} GB/s", file=sys.stderr, flush=True)
         del host_pool
+        # The same step with the sharing-aware decode: each group's shared
+        # prompt blocks are read once for all of its samples.
+        first = case.block_tables[:, 0]
+        groups = [np.flatnonzero(first == b).tolist() for b in np.unique(first)]
+        gm, gp, st, maxp = pa.shared_prefix_groups(case.block_tables, case.context_lens, groups, B)
+        gm_d, gp_d, st_d = to_dev(gm), to_dev(gp), to_dev(st)
+        wss = pa.alloc_decode_shared_workspace(S, H, D, max_ctx, B, gm.shape[0], maxp, workers, device=dev)
+
+        def shared_step(i, ev=None):
+            k_cache, v_cache = pools[i % len(pools)]
+            pa.copy_blocks([k_cache], [v_cache], mapping)
+            if ev is not None:
+                ev[0].record(stream)
+            pa.paged_attention_decode_shared(out, q, k_cache, v_cache, block_tables, context_lens, max_ctx,
+                                             case.scale, gm_d, gp_d, st_d, maxp, workspace=wss,
+                                             split_workers=workers)
+            if ev is not None:
+                ev[1].record(stream)
+
+        for i in range(args.warmup):
+            shared_step(i)
+        sh_ms, _ = timed_steps(torch, shared_step, args, len(pools))
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):
+            shared_step(i, sev[i])
+        torch.cuda.synchronize()
+        dec_ms = [a.elapsed_time(z) for a, z in sev]
+        dec_s = float(np.mean(dec_ms)) * 1e-3
+        distinct = len({b for blocks in case.seq_blocks for b in blocks}) * 2 * row * B
+        components["decode_shared"] = {
+            "groups": int(gm.shape[0]), "shared_prefix_tokens": int(maxp), "step_us": sh_ms * 1e3,
+            "tokens_per_s": S / (sh_ms * 1e-3), "decode_call_avg_us": dec_s * 1e6, **launch_stats(dec_ms),
+            "logical_kv_gbps": kv_bytes / dec_s / 1e9, "distinct_kv_gbps": distinct / dec_s / 1e9}
+        print(f"[bench] shared-prefix decode: step {sh_ms * 1e3:.1f} us ({S / (sh_ms * 1e-3):.0f} tokens/s); "
+              f"decode call {dec_s * 1e6:.1f} us, {distinct / dec_s / 1e9:.0f} GB/s of distinct blocks",
+              file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
