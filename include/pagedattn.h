@@ -17,8 +17,12 @@
  *
  * Conventions for every call
  *  - All data pointers are DEVICE pointers allocated by the caller (e.g. by
- *    PyTorch); the library keeps no pointer after a call returns, allocates
- *    nothing, and holds no mutable global state: calls are re-entrant.
+ *    PyTorch), except where a call says otherwise (host pointer arrays of
+ *    pa_copy_blocks and pa_swap_blocks, pinned host pools of pa_swap_blocks,
+ *    the host-only block manager).  The library keeps no pointer after a
+ *    call returns, allocates no device memory, and holds no mutable global
+ *    state: calls are re-entrant (a block manager is an object of its own,
+ *    created and destroyed by the caller).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on that stream and returns without synchronising.
  *  - Layouts are C-contiguous:
