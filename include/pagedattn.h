@@ -34,10 +34,10 @@
  *    position p of a sequence is block_tables[s][p / B] * B + p % B
  *    ("KV 캐시 관리와 PagedAttention", llm-systems-engineering.pages.dev,
  *    section on linking token order to storage).
- *  - Supported shapes: head_dim 64 or 128; block_size 4, 8, 16, 32 or 64
- *    (the prefill chunk: 4 to 32); dtype fp32, fp16 or bf16 (the prefill
- *    chunk: fp16/bf16, head_dim 128).  All data pointers must be 16-byte
- *    aligned.
+ *  - Supported shapes: head_dim 64 or 128; block_size 4, 8, 16, 32 or 64;
+ *    dtype fp32, fp16 or bf16 (the prefill chunk: fp16/bf16, head_dim 128;
+ *    the shared-prefix decode: block_size 16 to 64).  All data pointers must
+ *    be 16-byte aligned.
  *  - Errors are found by synchronous host checks on the scalar arguments and
  *    pointers (never on device data).  On any error the call returns a
  *    non-zero status, enqueues nothing and writes nothing; pa_last_error()

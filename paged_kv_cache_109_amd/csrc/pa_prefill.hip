@@ -530,7 +530,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_chunk_kernel(PrefillArg
 
 bool prefill_supported(int dtype, int head_dim, int block_size) {
   const bool dt = dtype == (int)Dt::F16 || dtype == (int)Dt::BF16;
-  const bool b = block_size == 4 || block_size == 8 || block_size == 16 || block_size == 32;
+  const bool b = block_size == 4 || block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64;
   return dt && head_dim == kPfD && b;
 }
 
@@ -557,6 +557,7 @@ static hipError_t launch_pf_b(const PrefillArgs &a, int B, hipStream_t st) {
     case 8: return launch_pf<T, 8>(a, st);
     case 16: return launch_pf<T, 16>(a, st);
     case 32: return launch_pf<T, 32>(a, st);
+    case 64: return launch_pf<T, 64>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -39,7 +39,7 @@ def run_prefill(c, poison=False):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("B", [4, 8, 16, 32])
+@pytest.mark.parametrize("B", [4, 8, 16, 32, 64])
 def test_prefill_shapes(dtype, B):
     c = W.make_prefill_case(4, 0, [0, 37, 300, 5], 3, 128, B, dtype, seed=B, q_lens=[5, 130, 256, 1],
                             name=f"prefill_B{B}")
