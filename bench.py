@@ -69,11 +69,14 @@ def committed_traffic(profile: str, source: str = "pa_decode.hip"):
     the current kernel source."""
     path = os.path.join(ROOT, "profiles", f"{profile}_counters.md")
     if not os.path.exists(path):
+        print(f"[bench] no counter summary {os.path.basename(path)}: traffic = null", file=sys.stderr)
         return None
     text = open(path).read()
     m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m or not t or m.group(1) != kernel_source_digest(source):
+        print(f"[bench] {os.path.basename(path)} was taken on another {source} "
+              f"({m.group(1) if m else '?'} vs {kernel_source_digest(source)}): traffic = null", file=sys.stderr)
         return None
     return float(t.group(1))
 
