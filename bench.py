@@ -49,6 +49,8 @@ def parse():
                     help="copies of the KV pool used in turn, so no step finds the last one's data in cache")
     ap.add_argument("--split-workers", type=int, default=0,
                     help="worker waves the tile stream is cut among (0: as many as the GPU holds)")
+    ap.add_argument("--dtype", default=None, choices=["f16", "bf16", "f32"],
+                    help="element type of the decode workloads (default: the workload's own, fp16)")
     ap.add_argument("--block-size", type=int, default=16,
                     help="tokens per KV block for the decode workloads (4, 8, 16, 32 or 64)")
     ap.add_argument("--graph", action="store_true",
@@ -184,8 +186,9 @@ def main():
             sys.exit(2)
         return bench_prefill(args)
     t0 = time.time()
+    extra = {"dtype": args.dtype} if args.dtype else {}
     case = {"opt13b_b64": W.opt13b_b64, "large_batch_b256": W.large_batch_b256,
-            "parallel_sampling": W.parallel_sampling}[args.workload](block_size=args.block_size)
+            "parallel_sampling": W.parallel_sampling}[args.workload](block_size=args.block_size, **extra)
     print(f"[bench] workload {case.name} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
@@ -265,7 +268,8 @@ def main():
     achieved = alg_bytes / part_avg_s / 1e9
     tokens_per_s = S / (ms_per_step * 1e-3)
     # Counter summaries are committed for the 16-token-block workloads only.
-    traffic = committed_traffic("decode_partition_" + case.name.rsplit("_", 1)[0]) if B == 16 else None
+    traffic = (committed_traffic("decode_partition_" + case.name.rsplit("_", 1)[0])
+               if B == 16 and case.dtype == "f16" else None)
 
     # The other kernels of the step, each timed by its own events: algorithmic
     # bytes are what the call must read plus what it must write.

@@ -99,12 +99,6 @@ __device__ __forceinline__ float other_half(float x) {
 
 __device__ __forceinline__ uint4 load16(const char *p) { return *reinterpret_cast<const uint4 *>(p); }
 
-// A value no later code reads: the register holding it is free from here.
-__device__ __forceinline__ uint4 forget(const uint4 &v) {
-  return make_uint4(__builtin_nondeterministic_value(v.x), __builtin_nondeterministic_value(v.y),
-                    __builtin_nondeterministic_value(v.z), __builtin_nondeterministic_value(v.w));
-}
-
 
 }  // namespace
 
