@@ -213,12 +213,25 @@ pa_status pa_paged_attention_decode_reduce(void *out, const int32_t *context_len
  *  max_prefix_len host upper bound of group_prefix.
  *  workspace      >= pa_decode_shared_workspace_bytes(...) bytes, 16-byte
  *                 aligned; needs no initialisation.
+ *  phases         which of the three steps this call enqueues: PA_SHARED_OWN
+ *                 (each sequence's own positions: the stream-K pass and its
+ *                 fix-up), PA_SHARED_PREFIX (the groups' shared prefixes),
+ *                 PA_SHARED_COMBINE (the merge into out); PA_SHARED_ALL runs
+ *                 them in order on `stream`.  OWN and PREFIX read disjoint
+ *                 data and write disjoint parts of the workspace, so a caller
+ *                 may enqueue them on two streams to run at once; COMBINE
+ *                 must follow both (e.g. after an event join).  Every call of
+ *                 one decode passes the same arguments and workspace.
  * Other arguments as for pa_paged_attention_decode.  block_size 16, 32 or
  * 64 (PA_ERR_UNSUPPORTED otherwise).  The group description is not checked
  * against the tables on the host (that needs device data); an inconsistent
  * one gives wrong results, never an access outside the given arrays.
  */
 #define PA_MAX_GROUP_MEMBERS 8
+#define PA_SHARED_OWN 1
+#define PA_SHARED_PREFIX 2
+#define PA_SHARED_COMBINE 4
+#define PA_SHARED_ALL 7
 size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                         int32_t max_context_len, int32_t block_size,
                                         int32_t num_groups, int32_t max_prefix_len,
@@ -229,7 +242,7 @@ pa_status pa_paged_attention_decode_shared(
     int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
     float scale, pa_dtype dtype, const int32_t *group_members, const int32_t *group_prefix,
     const int32_t *seq_starts, int32_t num_groups, int32_t max_prefix_len, int32_t split_workers,
-    void *workspace, size_t workspace_bytes, void *stream);
+    int32_t phases, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * pa_copy_blocks -- batched whole-block copy for copy-on-write.

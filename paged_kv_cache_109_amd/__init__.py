@@ -11,6 +11,10 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     OutOfBlocks,
     STREAM_SINK_WORDS_PER_GROUP,
+    SHARED_ALL,
+    SHARED_COMBINE,
+    SHARED_OWN,
+    SHARED_PREFIX,
     PagedAttnError,
     abi_version,
     MAX_GROUP_MEMBERS,

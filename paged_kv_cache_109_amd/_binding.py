@@ -46,8 +46,8 @@ _SIGS = {
     "pa_swap_blocks": ([P, P, i32, P, i64, i64, i64, i64, P], ctypes.c_int),
     "pa_decode_shared_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32, i32], sz),
     "pa_paged_attention_decode_shared": (
-        [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, P, P, P, i32, i32, i32, P, sz, P],
-        ctypes.c_int),
+        [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, P, P, P, i32, i32, i32, i32, P, sz,
+         P], ctypes.c_int),
     "pa_bm_create": ([i64, i32, i32, P, P], ctypes.c_int),
     "pa_bm_destroy": ([P], None),
     "pa_bm_num_free": ([P], i64),
@@ -189,6 +189,7 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
 
 
 MAX_GROUP_MEMBERS = 8
+SHARED_OWN, SHARED_PREFIX, SHARED_COMBINE, SHARED_ALL = 1, 2, 4, 7
 
 
 def alloc_decode_shared_workspace(num_seqs, num_heads, head_dim, max_context_len, block_size, num_groups,
@@ -204,13 +205,15 @@ def paged_attention_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: t
                                   scale: float, group_members: torch.Tensor, group_prefix: torch.Tensor,
                                   seq_starts: torch.Tensor, max_prefix_len: int,
                                   workspace: Optional[torch.Tensor] = None, split_workers: int = 0,
-                                  stream=None) -> torch.Tensor:
+                                  stream=None, phases: int = 7) -> torch.Tensor:
     """Decode where groups of sequences share the blocks of a prompt prefix:
     group_members int32 [G, 8] (sequence ids, -1 padded), group_prefix int32
     [G] (shared tokens), seq_starts int32 [S] (the prefix of a sequence's
     group, else 0), all device tensors -- see sharing.shared_prefix_groups.
     Same result as paged_attention_decode; each shared block is read once
-    per group."""
+    per group. phases (SHARED_OWN | SHARED_PREFIX | SHARED_COMBINE) picks the
+    steps this call enqueues; the first two may run on two streams at once,
+    the combine after both (same workspace for all three calls)."""
     G = int(group_members.shape[0])
     if group_members.dim() != 2 or group_members.shape[1] != MAX_GROUP_MEMBERS or group_prefix.shape != (G,):
         raise ValueError(f"group_members must be [groups, {MAX_GROUP_MEMBERS}] and group_prefix [groups]")
@@ -227,8 +230,8 @@ def paged_attention_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: t
     ws_ptr, ws_bytes, st = args[-3:]
     _check(_lib.pa_paged_attention_decode_shared(
         *args[:15], _dev(group_members, "group_members", torch.int32), _dev(group_prefix, "group_prefix", torch.int32),
-        _dev(seq_starts, "seq_starts", torch.int32), G, int(max_prefix_len), int(split_workers), ws_ptr, ws_bytes,
-        st), "paged_attention_decode_shared")
+        _dev(seq_starts, "seq_starts", torch.int32), G, int(max_prefix_len), int(split_workers), int(phases), ws_ptr,
+        ws_bytes, st), "paged_attention_decode_shared")
     return out
 
 

@@ -373,8 +373,8 @@ pa_status pa_paged_attention_decode_shared(void *out, const void *q, const void 
                                            int64_t num_blocks, float scale, pa_dtype dtype,
                                            const int32_t *group_members, const int32_t *group_prefix,
                                            const int32_t *seq_starts, int32_t num_groups, int32_t max_prefix_len,
-                                           int32_t split_workers, void *workspace, size_t workspace_bytes,
-                                           void *stream) {
+                                           int32_t split_workers, int32_t phases, void *workspace,
+                                           size_t workspace_bytes, void *stream) {
   pa_status st = check_decode_common(k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                                      max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks,
                                      dtype, split_workers);
@@ -384,6 +384,8 @@ pa_status pa_paged_attention_decode_shared(void *out, const void *q, const void 
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
   if (num_groups < 0 || max_prefix_len < 0)
     return fail(PA_ERR_INVALID_ARG, "num_groups and max_prefix_len must be >= 0");
+  if (phases <= 0 || (phases & ~PA_SHARED_ALL) != 0)
+    return fail(PA_ERR_INVALID_ARG, "phases must be a non-empty mask of PA_SHARED_OWN/PREFIX/COMBINE");
   if (num_seqs > 0 && (!out || !q || !seq_starts)) return fail(PA_ERR_INVALID_ARG, "null out, q or seq_starts");
   if (num_groups > 0 && (!group_members || !group_prefix))
     return fail(PA_ERR_INVALID_ARG, "null group_members or group_prefix");
@@ -401,10 +403,12 @@ pa_status pa_paged_attention_decode_shared(void *out, const void *q, const void 
   a.starts = seq_starts;
   a.suffix_out = reinterpret_cast<float *>(ws + g.suffix_off);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  st = hip_status(pa::launch_decode_partitions(a, dtype, head_dim, block_size, s), "decode partitions");
-  if (st != PA_OK) return st;
-  st = hip_status(pa::launch_decode_reduce(a, dtype, head_dim, s), "decode reduce");
-  if (st != PA_OK) return st;
+  if (phases & PA_SHARED_OWN) {
+    st = hip_status(pa::launch_decode_partitions(a, dtype, head_dim, block_size, s), "decode partitions");
+    if (st != PA_OK) return st;
+    st = hip_status(pa::launch_decode_reduce(a, dtype, head_dim, s), "decode reduce");
+    if (st != PA_OK) return st;
+  }
   pa::SharedArgs sa;
   sa.out = out;
   sa.q = q;
@@ -427,7 +431,9 @@ pa_status pa_paged_attention_decode_shared(void *out, const void *q, const void 
   sa.ctx_cap = g.dec.ctx_cap;
   sa.suffix_row = a.suffix_row;
   sa.scale_log2 = a.scale_log2;
-  return hip_status(pa::launch_shared_prefix_and_combine(sa, dtype, head_dim, block_size, s), "shared prefix");
+  return hip_status(pa::launch_shared_phases(sa, dtype, head_dim, block_size, (phases & PA_SHARED_PREFIX) != 0,
+                                             (phases & PA_SHARED_COMBINE) != 0, s),
+                    "shared prefix");
 }
 
 pa_status pa_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t num_layers,

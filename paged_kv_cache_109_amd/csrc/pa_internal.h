@@ -131,8 +131,8 @@ struct SharedArgs {
 };
 
 bool shared_supported(int dtype, int head_dim, int block_size);
-hipError_t launch_shared_prefix_and_combine(const SharedArgs &a, int dtype, int head_dim, int block_size,
-                                            hipStream_t stream);
+hipError_t launch_shared_phases(const SharedArgs &a, int dtype, int head_dim, int block_size, bool prefix,
+                                bool combine, hipStream_t stream);
 
 bool prefill_supported(int dtype, int head_dim, int block_size);
 hipError_t launch_prefill_chunk(const PrefillArgs &a, int dtype, int head_dim, int block_size,

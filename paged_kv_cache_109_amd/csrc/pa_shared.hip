@@ -269,19 +269,21 @@ hipError_t launch_prefix_td(const SharedArgs &a, int B, hipStream_t st) {
 }
 
 template <Dt T>
-hipError_t launch_shared_t(const SharedArgs &a, int D, int B, hipStream_t st) {
+hipError_t launch_shared_t(const SharedArgs &a, int D, int B, bool prefix, bool combine, hipStream_t st) {
   const int64_t items = (int64_t)a.num_groups * kSharedMaxMembers * a.num_heads;
   const dim3 grid((unsigned)((items + kDecodeWavesPerGroup - 1) / kDecodeWavesPerGroup));
   const dim3 block(kDecodeWavesPerGroup * kWave);
-  hipError_t e = hipErrorInvalidValue;
-  if (D == 64) {
-    e = launch_prefix_td<T, 64>(a, B, st);
-    if (e == hipSuccess) hipLaunchKernelGGL((decode_combine_kernel<T, 64>), grid, block, 0, st, a);
-  } else if (D == 128) {
-    e = launch_prefix_td<T, 128>(a, B, st);
-    if (e == hipSuccess) hipLaunchKernelGGL((decode_combine_kernel<T, 128>), grid, block, 0, st, a);
+  if (D != 64 && D != 128) return hipErrorInvalidValue;
+  if (prefix) {
+    const hipError_t e = D == 64 ? launch_prefix_td<T, 64>(a, B, st) : launch_prefix_td<T, 128>(a, B, st);
+    if (e != hipSuccess) return e;
   }
-  return e == hipSuccess ? hipGetLastError() : e;
+  if (combine) {
+    if (D == 64) hipLaunchKernelGGL((decode_combine_kernel<T, 64>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((decode_combine_kernel<T, 128>), grid, block, 0, st, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -291,13 +293,13 @@ bool shared_supported(int dtype, int head_dim, int block_size) {
          (block_size == 16 || block_size == 32 || block_size == 64);
 }
 
-hipError_t launch_shared_prefix_and_combine(const SharedArgs &a, int dtype, int head_dim, int block_size,
-                                            hipStream_t stream) {
-  if (a.num_groups == 0) return hipSuccess;
+hipError_t launch_shared_phases(const SharedArgs &a, int dtype, int head_dim, int block_size, bool prefix,
+                                bool combine, hipStream_t stream) {
+  if (a.num_groups == 0 || (!prefix && !combine)) return hipSuccess;
   switch (static_cast<Dt>(dtype)) {
-    case Dt::F32: return launch_shared_t<Dt::F32>(a, head_dim, block_size, stream);
-    case Dt::F16: return launch_shared_t<Dt::F16>(a, head_dim, block_size, stream);
-    case Dt::BF16: return launch_shared_t<Dt::BF16>(a, head_dim, block_size, stream);
+    case Dt::F32: return launch_shared_t<Dt::F32>(a, head_dim, block_size, prefix, combine, stream);
+    case Dt::F16: return launch_shared_t<Dt::F16>(a, head_dim, block_size, prefix, combine, stream);
+    case Dt::BF16: return launch_shared_t<Dt::BF16>(a, head_dim, block_size, prefix, combine, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -133,14 +133,15 @@ def test_shared_decode_rejects_bad_arguments():
     f = B._lib.pa_paged_attention_decode_shared
 
     def call(**over):
-        a = dict(Bs=16, members=FAKE, prefix=FAKE, starts=FAKE, G=1, maxp=32, ws=None, ws_bytes=0)
+        a = dict(Bs=16, members=FAKE, prefix=FAKE, starts=FAKE, G=1, maxp=32, phases=7, ws=None, ws_bytes=0)
         a.update(over)
         return f(FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 100, 2, 4, 128, a["Bs"], 64, 0.1, 1, a["members"],
-                 a["prefix"], a["starts"], a["G"], a["maxp"], 0, a["ws"], a["ws_bytes"], None)
+                 a["prefix"], a["starts"], a["G"], a["maxp"], 0, a["phases"], a["ws"], a["ws_bytes"], None)
     assert call(Bs=8) == 2              # blocks of 8 are not built for the shared path
     assert call(members=None) == 1      # groups without members
     assert call(starts=None) == 1
     assert call(G=-1) == 1
+    assert call(phases=0) == 1 and call(phases=8) == 1
     assert call() == 3                  # workspace missing
     n = B._lib.pa_decode_shared_workspace_bytes
     assert n(2, 4, 128, 100, 16, 1, 32, 7) > B._lib.pa_decode_workspace_bytes(2, 4, 128, 100, 16, 7)

@@ -111,3 +111,27 @@ def test_full_size_parallel_sampling_shared_matches_plain_decode():
     ref = oracle.decode(c.q, k, v, c.block_tables, c.context_lens, c.scale, c.dtype)
     check_attention(out, ref, c.dtype, "parallel_sampling shared")
     check_attention(plain, ref, c.dtype, "parallel_sampling plain")
+
+
+def test_phases_on_two_streams_equal_the_single_call():
+    """The own-position pass and the prefix phase enqueued on two streams
+    at once, the combine after both: bit-identical to one call."""
+    q, k, v, tables, lens, groups = build("bf16", 128, 16, SPEC, singles=[9, 300], seed=77)
+    one, _ = run_shared(q, k, v, tables, lens, groups, 16, "bf16")
+    gm, gp, st, maxp = pa.shared_prefix_groups(tables, lens, groups, 16)
+    args = (dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(tables), dev(lens), int(lens.max()), D_SCALE[128],
+            dev(gm), dev(gp), dev(st), maxp)
+    ws = pa.alloc_decode_shared_workspace(len(lens), 3, 128, int(lens.max()), 16, len(gm), maxp)
+    out = torch.full_like(one, float("nan"))
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    side.wait_stream(main)
+    say("  shared decode phases on two streams")
+    for rep in range(3):
+        pa.paged_attention_decode_shared(out, *args, workspace=ws, phases=pa.SHARED_OWN)
+        with torch.cuda.stream(side):
+            pa.paged_attention_decode_shared(out, *args, workspace=ws, phases=pa.SHARED_PREFIX)
+        main.wait_stream(side)
+        pa.paged_attention_decode_shared(out, *args, workspace=ws, phases=pa.SHARED_COMBINE)
+        side.wait_stream(main)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), one.view(torch.int16)), f"repeat {rep}"
