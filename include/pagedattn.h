@@ -35,9 +35,8 @@
  *    ("KV 캐시 관리와 PagedAttention", llm-systems-engineering.pages.dev,
  *    section on linking token order to storage).
  *  - Supported shapes: head_dim 64 or 128; block_size 4, 8, 16, 32 or 64;
- *    dtype fp32, fp16 or bf16 (the prefill chunk: fp16/bf16, head_dim 128;
- *    the shared-prefix decode: block_size 16 to 64).  All data pointers must
- *    be 16-byte aligned.
+ *    dtype fp32, fp16 or bf16 (the shared-prefix decode: block_size 16 to
+ *    64).  All data pointers must be 16-byte aligned.
  *  - Errors are found by synchronous host checks on the scalar arguments and
  *    pointers (never on device data).  On any error the call returns a
  *    non-zero status, enqueues nothing and writes nothing; pa_last_error()
@@ -279,7 +278,11 @@ pa_status pa_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t n
  * starts at c = context_lens[s] - q_len and query j attends, with the same
  * softmax as decode, to positions 0 .. c+j.
  *
- *  out, q          device [total_q][num_heads][head_dim], fp16 or bf16.
+ * fp16 and bf16 at head_dim 128 run on the matrix cores (MFMA); fp32, and
+ * head_dim 64, run on the vector ALU (8 queries per wave, each K/V tile read
+ * once for them).
+ *
+ *  out, q          device [total_q][num_heads][head_dim], `dtype`.
  *  cu_q_lens       device int32 [num_seqs + 1], non-decreasing, from 0 to
  *                  total_q.
  *  max_q_len       host bound of the per-sequence q_len.

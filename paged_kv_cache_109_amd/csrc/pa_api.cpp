@@ -467,7 +467,7 @@ pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32
       block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
     return fail(PA_ERR_INVALID_ARG, "sizes must be positive (num_seqs, total_q, max_q_len, max_context_len >= 0)");
   if (!pa::prefill_supported(dtype, head_dim, block_size))
-    return fail(PA_ERR_UNSUPPORTED, "prefill chunk is built for fp16/bf16, head_dim 128, block_size 16/32 "
+    return fail(PA_ERR_UNSUPPORTED, "prefill chunk is built for head_dim 64/128 and block_size 4/8/16/32/64 "
                 "(got dtype %d, head_dim %d, block_size %d)", dtype, head_dim, block_size);
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");

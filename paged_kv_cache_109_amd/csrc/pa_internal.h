@@ -135,6 +135,9 @@ hipError_t launch_shared_phases(const SharedArgs &a, int dtype, int head_dim, in
                                 bool combine, hipStream_t stream);
 
 bool prefill_supported(int dtype, int head_dim, int block_size);
+// fp32 and head_dim 64 prefill (pa_prefill_general.hip).
+bool prefill_general_supported(int dtype, int head_dim, int block_size);
+hipError_t launch_prefill_general(const PrefillArgs &a, int dtype, int head_dim, int block_size, hipStream_t stream);
 hipError_t launch_prefill_chunk(const PrefillArgs &a, int dtype, int head_dim, int block_size,
                                 hipStream_t stream);
 

@@ -522,7 +522,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_chunk_kernel(PrefillArg
   }
 }
 
-bool prefill_supported(int dtype, int head_dim, int block_size) {
+static bool prefill_mfma_supported(int dtype, int head_dim, int block_size) {
   const bool dt = dtype == (int)Dt::F16 || dtype == (int)Dt::BF16;
   const bool b = block_size == 4 || block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64;
   return dt && head_dim == kPfD && b;
@@ -556,11 +556,20 @@ static hipError_t launch_pf_b(const PrefillArgs &a, int B, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+bool prefill_supported(int dtype, int head_dim, int block_size) {
+  return prefill_mfma_supported(dtype, head_dim, block_size) || prefill_general_supported(dtype, head_dim, block_size);
+}
+
 hipError_t launch_prefill_chunk(const PrefillArgs &a, int dtype, int head_dim, int block_size, hipStream_t stream) {
-  if (!prefill_supported(dtype, head_dim, block_size)) return hipErrorInvalidValue;
   if (a.num_seqs == 0 || a.max_q_len == 0) return hipSuccess;
-  if (dtype == (int)Dt::BF16) return launch_pf_b<Dt::BF16>(a, block_size, stream);
-  return launch_pf_b<Dt::F16>(a, block_size, stream);
+  if (prefill_mfma_supported(dtype, head_dim, block_size)) {
+    if (dtype == (int)Dt::BF16) return launch_pf_b<Dt::BF16>(a, block_size, stream);
+    return launch_pf_b<Dt::F16>(a, block_size, stream);
+  }
+  // fp32, or head_dim 64: the vector-ALU kernel.
+  if (prefill_general_supported(dtype, head_dim, block_size))
+    return launch_prefill_general(a, dtype, head_dim, block_size, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

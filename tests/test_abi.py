@@ -97,7 +97,8 @@ def test_copy_blocks_rejects_bad_arguments():
 
 def test_prefill_rejects_unsupported_shapes():
     f = B._lib.pa_paged_attention_prefill_chunk
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 10, 5, 100, 4, 64, 16, 64, 0.1, 0, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 10, 5, 100, 4, 96, 16, 64, 0.1, 0, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 10, 5, 100, 4, 128, 12, 64, 0.1, 1, None) == 2
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.1, float("nan"), float("inf")])

@@ -47,6 +47,25 @@ def test_prefill_shapes(dtype, B):
     say("  max err", check_attention(out, ref, dtype, c.name))
 
 
+@pytest.mark.parametrize("dtype,D", [("f32", 128), ("f32", 64), ("f16", 64), ("bf16", 64)])
+@pytest.mark.parametrize("B", [4, 16, 64])
+def test_prefill_general_shapes(dtype, D, B):
+    """fp32 and head_dim 64 run on the vector-ALU prefill kernel (8 queries
+    per wave): ragged chunks (1, 5, 9, 130 queries) after 0..300 cached
+    tokens, one chunk longer than its 8-query groups by one."""
+    c = W.make_prefill_case(4, 0, [0, 37, 300, 5], 3, D, B, dtype, seed=B + D, q_lens=[5, 130, 9, 1],
+                            name=f"prefill_general_{dtype}_D{D}_B{B}")
+    out, ref = run_prefill(c)
+    say("  max err", check_attention(out, ref, dtype, c.name))
+
+
+def test_prefill_general_poisoned_slots_are_never_read():
+    c = W.make_prefill_case(3, 0, [17, 0, 64], 2, 64, 16, "f16", seed=9, q_lens=[40, 33, 17], name="poison64")
+    out, ref = run_prefill(c, poison=True)
+    assert not torch.isnan(out).any()
+    check_attention(out, ref, "f16", "poisoned, head_dim 64")
+
+
 def test_prefill_poisoned_slots_are_never_read():
     c = W.make_prefill_case(3, 0, [17, 0, 64], 2, 128, 16, "bf16", seed=5, q_lens=[40, 33, 128], name="poison")
     # Poison everything outside the final contexts; the chunk tokens are written
