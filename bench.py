@@ -56,7 +56,8 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the step captured as a HIP graph instead of eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-runs", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the CPU oracle on the batch until this much time has passed (at least 3 runs)")
     return ap.parse_args()
 
 
@@ -158,6 +159,17 @@ def timed_steps(torch, step, args, n_replicas):
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / args.steps, ("hip graph replay" if graphs else "eager launches")
+
+
+def time_oracle(fn, seconds: float):
+    """Run fn repeatedly for at least `seconds` (and at least 3 times);
+    return the per-run times."""
+    times, start = [], time.perf_counter()
+    while len(times) < 3 or time.perf_counter() - start < seconds:
+        t = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t)
+    return times
 
 
 def launch_stats(ms):
@@ -371,17 +383,15 @@ def main():
         import oracle
         oracle.load()
         threads = len(os.sched_getaffinity(0))
-        times = []
-        for _ in range(args.cpu_runs):
-            t = time.perf_counter()
-            oracle.decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens, case.scale,
-                          case.dtype, threads=threads)
-            times.append(time.perf_counter() - t)
+        times = time_oracle(lambda: oracle.decode(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                                  case.context_lens, case.scale, case.dtype, threads=threads),
+                            args.cpu_seconds)
         t_med = float(np.median(times))
         cpu = {"value": S / t_med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"the whole {case.name} batch ({S} seqs, {int(case.context_lens.sum())} context tokens, "
-                         f"{H} heads) decoded {args.cpu_runs} times by the fp64 C oracle with OpenMP over "
-                         f"(seq, head); median {t_med:.2f}s; CPU {platform.processor() or platform.machine()}",
+                         f"{H} heads) decoded {len(times)} times ({sum(times):.1f}s) by the fp64 C oracle with "
+                         f"OpenMP over (seq, head); median {t_med:.2f}s per batch; CPU "
+                         f"{platform.processor() or platform.machine()}",
                "effective_kv_gbps": kv_bytes / t_med / 1e9}
 
     result = {
@@ -485,13 +495,13 @@ def bench_prefill(args):
     if not args.no_cpu_baseline:
         import oracle
         threads = len(os.sched_getaffinity(0))
-        t = time.perf_counter()
-        oracle.prefill_chunk(case.q, case.cu_q_lens, case.k_cache, case.v_cache, case.block_tables,
-                             case.context_lens, case.scale, case.dtype, threads=threads)
-        dt_cpu = time.perf_counter() - t
+        times = time_oracle(lambda: oracle.prefill_chunk(case.q, case.cu_q_lens, case.k_cache, case.v_cache,
+                                                         case.block_tables, case.context_lens, case.scale,
+                                                         case.dtype, threads=threads), args.cpu_seconds)
+        dt_cpu = float(np.median(times))
         cpu = {"value": int(q_lens.sum()) / dt_cpu, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
-               "sample": f"the whole chunked_prefill batch ({S} x {max_q} queries, {H} heads) once by the fp64 C "
-                         f"oracle; {dt_cpu:.2f}s"}
+               "sample": f"the whole chunked_prefill batch ({S} x {max_q} queries, {H} heads) {len(times)} times "
+                         f"({sum(times):.1f}s) by the fp64 C oracle with OpenMP; median {dt_cpu:.2f}s per batch"}
     result = {
         "metric": "chunked prefill paged attention query tokens/s (MFMA), OPT-13B shapes",
         "value": int(q_lens.sum()) / (ms_per_step * 1e-3), "unit": "query tokens/s", "n_gpus": 1,
