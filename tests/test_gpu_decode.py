@@ -191,3 +191,13 @@ def test_opt13b_batch64_full_size():
     dc = DeviceCase(c)
     out = gpu_decode(dc)
     say("  max err", check_attention(out, ref_decode(c), "f16", c.name))
+
+
+@pytest.mark.parametrize("dtype,B", [("bf16", 16), ("f16", 64)])
+def test_long_contexts(dtype, B):
+    """Contexts of tens of thousands of tokens (a pair cut across many worker
+    waves) beside short ones."""
+    lens = [50001, 3, 32768, 777]
+    c = W.make_decode_case(len(lens), 2, 128, B, dtype, lens, seed=5, max_blocks_per_seq=W.blocks_needed(50001, B))
+    dc = DeviceCase(c)
+    check_attention(gpu_decode(dc), ref_decode(c), dtype, f"long contexts {dtype} B={B}")
