@@ -97,9 +97,9 @@ def test_chunked_prefill_full_size():
     say("  max err", check_attention(out, ref, "bf16", c.name))
 
 
-def test_prefill_context_longer_than_the_lds_table():
-    """More than 4096 table entries (16,640 tokens at B=4): the kernel reads
-    the block table from memory instead of its LDS copy."""
+def test_prefill_long_context_small_blocks():
+    """A 16,600-token context at B=4: over 4,000 table entries, each 4-row
+    load of a 32-key block on its own block."""
     c = W.make_prefill_case(2, 0, [16600, 3], 2, 128, 4, "bf16", seed=11, q_lens=[40, 7], name="long_table")
     out, ref = run_prefill(c)
     say("  max err", check_attention(out, ref, "bf16", c.name))
