@@ -50,6 +50,17 @@
  *    block contribute nothing; a slot outside the pool is skipped; a copy
  *    pair outside the pool is skipped; context lengths are clipped to
  *    [0, min(max_context_len, max_blocks_per_seq * block_size)].
+ *  - Debug validation: with PA_DEBUG_VALIDATE=1 in the environment, every
+ *    call that reads device index arrays (reshape_and_cache, the decode
+ *    calls but the reduce, decode_shared, copy_blocks, swap_blocks,
+ *    prefill_chunk) first synchronises `stream`, copies those arrays to the
+ *    host and checks the preconditions above -- and for decode_shared that
+ *    the groups match the tables, for prefill_chunk that cu_q_lens runs from
+ *    0 to total_q with every q_len within max_q_len and its context, for
+ *    swap_blocks that pairs lie in their pools with distinct destinations.
+ *    At the first violation it returns PA_ERR_INVALID_ARG, pa_last_error()
+ *    naming it, and enqueues nothing.  For debugging only: it blocks the
+ *    host and cannot run under stream capture (PA_ERR_HIP there).
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -222,9 +233,10 @@ pa_status pa_paged_attention_decode_reduce(void *out, const int32_t *context_len
  *                 must follow both (e.g. after an event join).  Every call of
  *                 one decode passes the same arguments and workspace.
  * Other arguments as for pa_paged_attention_decode.  block_size 16, 32 or
- * 64 (PA_ERR_UNSUPPORTED otherwise).  The group description is not checked
- * against the tables on the host (that needs device data); an inconsistent
- * one gives wrong results, never an access outside the given arrays.
+ * 64 (PA_ERR_UNSUPPORTED otherwise).  The group description is checked
+ * against the tables only under PA_DEBUG_VALIDATE=1 (that needs device
+ * data); an inconsistent one gives wrong results, never an access outside
+ * the given arrays.
  */
 #define PA_MAX_GROUP_MEMBERS 8
 #define PA_SHARED_OWN 1

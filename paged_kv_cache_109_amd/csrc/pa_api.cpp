@@ -1,6 +1,7 @@
 // C-ABI entry points of libpagedattn: argument checks, partition sizing and
 // dispatch to the kernel launchers.  Every check here is on host scalars and
-// pointer values; device data is never read.  On any failed check nothing is
+// pointer values; device data is read only in the debug validation
+// (PA_DEBUG_VALIDATE=1, pa_validate.cpp).  On any failed check nothing is
 // enqueued.
 #include "../../include/pagedattn.h"
 
@@ -255,6 +256,11 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, int64_t key_t
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PA_ERR_INVALID_ARG, "key, value and caches must be 16-byte aligned");
+  if (pa::debug_validate()) {
+    const pa_status vs = pa::validate_slots(slot_mapping, num_tokens, num_blocks, block_size,
+                                            reinterpret_cast<hipStream_t>(stream));
+    if (vs != PA_OK) return vs;
+  }
   return hip_status(pa::launch_reshape_and_cache(key, value, key_token_stride * eb, value_token_stride * eb,
                                                  k_cache, v_cache, slot_mapping, num_tokens, num_heads,
                                                  (int32_t)row_bytes, block_size, num_blocks,
@@ -296,6 +302,11 @@ static pa_status decode_impl(bool run_parts, bool run_reduce, void *out, const v
   const pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                                        num_seqs, num_heads, head_dim, dtype, num_blocks, scale, g, workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (run_parts && pa::debug_validate()) {
+    st = pa::validate_decode(block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs, block_size,
+                             num_blocks, s);
+    if (st != PA_OK) return st;
+  }
   if (run_parts) {
     st = hip_status(pa::launch_decode_partitions(a, dtype, head_dim, block_size, s), "decode partitions");
     if (st != PA_OK) return st;
@@ -403,6 +414,11 @@ pa_status pa_paged_attention_decode_shared(void *out, const void *q, const void 
   a.starts = seq_starts;
   a.suffix_out = reinterpret_cast<float *>(ws + g.suffix_off);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (pa::debug_validate()) {
+    st = pa::validate_shared(block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs, block_size,
+                             num_blocks, group_members, group_prefix, seq_starts, num_groups, max_prefix_len, s);
+    if (st != PA_OK) return st;
+  }
   if (phases & PA_SHARED_OWN) {
     st = hip_status(pa::launch_decode_partitions(a, dtype, head_dim, block_size, s), "decode partitions");
     if (st != PA_OK) return st;
@@ -450,6 +466,11 @@ pa_status pa_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t n
     if (!aligned16(k_caches[l]) || !aligned16(v_caches[l]))
       return fail(PA_ERR_INVALID_ARG, "layer %d: caches must be 16-byte aligned", l);
   }
+  if (pa::debug_validate()) {
+    const pa_status vs =
+        pa::validate_copy_pairs(block_mapping, num_pairs, num_blocks, reinterpret_cast<hipStream_t>(stream));
+    if (vs != PA_OK) return vs;
+  }
   return hip_status(pa::launch_copy_blocks(k_caches, v_caches, num_layers, block_mapping, num_pairs, block_bytes,
                                            num_blocks, reinterpret_cast<hipStream_t>(stream)),
                     "copy_blocks");
@@ -495,6 +516,12 @@ pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32
   if ((int64_t)max_blocks_per_seq * block_size < cap) cap = (int64_t)max_blocks_per_seq * block_size;
   a.ctx_cap = (int32_t)cap;
   a.scale_log2 = scale * kLog2e;
+  if (pa::debug_validate()) {
+    const pa_status vs = pa::validate_prefill(cu_q_lens, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                              total_q, max_q_len, max_context_len, block_size, num_blocks,
+                                              reinterpret_cast<hipStream_t>(stream));
+    if (vs != PA_OK) return vs;
+  }
   return hip_status(pa::launch_prefill_chunk(a, dtype, head_dim, block_size, reinterpret_cast<hipStream_t>(stream)),
                     "prefill chunk");
 }
@@ -520,6 +547,11 @@ pa_status pa_swap_blocks(const void *const *src_caches, void *const *dst_caches,
     dst[c] = const_cast<void *>(device_address(dst_caches[c]));
     if (!src[c] || !dst[c])
       return fail(PA_ERR_INVALID_ARG, "cache %d: caches must be device memory or pinned host memory", c);
+  }
+  if (pa::debug_validate()) {
+    const pa_status vs = pa::validate_swap_pairs(block_mapping, num_pairs, src_num_blocks, dst_num_blocks,
+                                                 reinterpret_cast<hipStream_t>(stream));
+    if (vs != PA_OK) return vs;
   }
   return hip_status(pa::launch_swap_blocks(src.data(), dst.data(), num_caches, mapping, num_pairs, block_bytes,
                                            src_num_blocks, dst_num_blocks, reinterpret_cast<hipStream_t>(stream)),

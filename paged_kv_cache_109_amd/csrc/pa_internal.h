@@ -138,6 +138,27 @@ bool prefill_supported(int dtype, int head_dim, int block_size);
 // fp32 and head_dim 64 prefill (pa_prefill_general.hip).
 bool prefill_general_supported(int dtype, int head_dim, int block_size);
 hipError_t launch_prefill_general(const PrefillArgs &a, int dtype, int head_dim, int block_size, hipStream_t stream);
+
+// Debug validation of the data-dependent preconditions (pa_validate.cpp):
+// active when PA_DEBUG_VALIDATE=1; each synchronises `stream`, reads the
+// index arrays to the host and returns PA_ERR_INVALID_ARG (with the
+// last-error record set) at the first violation.
+bool debug_validate();
+pa_status validate_slots(const int64_t *slot_mapping, int64_t num_tokens, int64_t num_blocks, int32_t block_size,
+                         hipStream_t stream);
+pa_status validate_decode(const int32_t *block_tables, int32_t max_blocks, const int32_t *context_lens,
+                          int32_t max_context_len, int32_t num_seqs, int32_t block_size, int64_t num_blocks,
+                          hipStream_t stream);
+pa_status validate_shared(const int32_t *block_tables, int32_t max_blocks, const int32_t *context_lens,
+                          int32_t max_context_len, int32_t num_seqs, int32_t block_size, int64_t num_blocks,
+                          const int32_t *group_members, const int32_t *group_prefix, const int32_t *seq_starts,
+                          int32_t num_groups, int32_t max_prefix_len, hipStream_t stream);
+pa_status validate_copy_pairs(const int64_t *block_mapping, int64_t num_pairs, int64_t num_blocks, hipStream_t stream);
+pa_status validate_swap_pairs(const int64_t *block_mapping, int64_t num_pairs, int64_t src_num_blocks,
+                              int64_t dst_num_blocks, hipStream_t stream);
+pa_status validate_prefill(const int32_t *cu_q_lens, const int32_t *block_tables, int32_t max_blocks,
+                           const int32_t *context_lens, int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                           int32_t max_context_len, int32_t block_size, int64_t num_blocks, hipStream_t stream);
 hipError_t launch_prefill_chunk(const PrefillArgs &a, int dtype, int head_dim, int block_size,
                                 hipStream_t stream);
 
