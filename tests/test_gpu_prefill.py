@@ -111,3 +111,45 @@ def test_prefill_three_query_tiles():
     c = W.make_prefill_case(2, 0, [1000, 0], 3, 128, 16, "f16", seed=12, q_lens=[300, 129], name="tiles")
     out, ref = run_prefill(c)
     say("  max err", check_attention(out, ref, "f16", c.name))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_mfma_chunks(seed):
+    """Seeded MFMA shapes: 1-8 sequences x 1-8 heads, chunks of 1 to 384
+    queries (one to four 128-query tiles, on and off the tile edges) after
+    0-3000 cached tokens, any block size, NaN in every slot outside a
+    context."""
+    rng = np.random.default_rng(3000 + seed)
+    S, H = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+    dtype = str(rng.choice(["f16", "bf16"]))
+    B = int(rng.choice([4, 8, 16, 32, 64]))
+    cached = [int(x) for x in rng.integers(0, 3001, size=S)]
+    cached[0] -= cached[0] % B  # one chunk starts on a block boundary
+    q_lens = [int(x) for x in rng.choice([1, 16, 63, 64, 65, 127, 128, 129, 255, 256, 300, 384], size=S)]
+    c = W.make_prefill_case(S, 0, cached, H, 128, B, dtype, seed=seed, q_lens=q_lens, name=f"mfma_{seed}")
+    out, ref = run_prefill(c, poison=True)
+    say("  max err", check_attention(out, ref, dtype, c.name))
+
+
+def test_permuting_physical_blocks_is_bit_identical():
+    """The same logical K/V in another physical placement gives the same
+    output bytes: the kernel's arithmetic follows logical positions only."""
+    c = W.make_prefill_case(3, 0, [100, 1000, 37], 4, 128, 16, "bf16", seed=21, q_lens=[200, 64, 129], name="perm")
+    slots = oracle.slots(c.block_tables, c.new_seq, c.new_pos, c.block_size)
+    oracle.reshape_and_cache(c.k_cache, c.v_cache, c.new_key, c.new_value, slots, c.dtype)
+    perm = np.random.default_rng(2).permutation(c.num_blocks)
+    k2 = np.empty_like(c.k_cache)
+    k2[perm] = c.k_cache
+    v2 = np.empty_like(c.v_cache)
+    v2[perm] = c.v_cache
+    bt2 = c.block_tables.copy()
+    for s, blks in enumerate(c.seq_blocks):
+        bt2[s, :len(blks)] = perm[np.asarray(blks)]
+    outs = []
+    for k, v, bt in ((c.k_cache, c.v_cache, c.block_tables), (k2, v2, bt2)):
+        out = torch.empty_like(dev(c.q, "bf16"))
+        pa.paged_attention_prefill_chunk(out, dev(c.q, "bf16"), dev(c.cu_q_lens), dev(k, "bf16"), dev(v, "bf16"),
+                                         dev(bt), dev(c.context_lens), 200, c.max_context_len, c.scale)
+        torch.cuda.synchronize()
+        outs.append(out.view(torch.int16))
+    assert torch.equal(outs[0], outs[1])
