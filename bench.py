@@ -161,6 +161,18 @@ def timed_steps(torch, step, args, n_replicas):
     return start.elapsed_time(end) / args.steps, ("hip graph replay" if graphs else "eager launches")
 
 
+
+def cpu_model() -> str:
+    """The host CPU's model name (for the oracle timing), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
 def time_oracle(fn, seconds: float):
     """Run fn repeatedly for at least `seconds` (and at least 3 times);
     return the per-run times."""
@@ -390,8 +402,7 @@ def main():
         cpu = {"value": S / t_med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"the whole {case.name} batch ({S} seqs, {int(case.context_lens.sum())} context tokens, "
                          f"{H} heads) decoded {len(times)} times ({sum(times):.1f}s) by the fp64 C oracle with "
-                         f"OpenMP over (seq, head); median {t_med:.2f}s per batch; CPU "
-                         f"{platform.processor() or platform.machine()}",
+                         f"OpenMP over (seq, head); median {t_med:.2f}s per batch; CPU {cpu_model()}",
                "effective_kv_gbps": kv_bytes / t_med / 1e9}
 
     result = {
@@ -501,7 +512,8 @@ def bench_prefill(args):
         dt_cpu = float(np.median(times))
         cpu = {"value": int(q_lens.sum()) / dt_cpu, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"the whole chunked_prefill batch ({S} x {max_q} queries, {H} heads) {len(times)} times "
-                         f"({sum(times):.1f}s) by the fp64 C oracle with OpenMP; median {dt_cpu:.2f}s per batch"}
+                         f"({sum(times):.1f}s) by the fp64 C oracle with OpenMP; median {dt_cpu:.2f}s per batch; "
+                         f"CPU {cpu_model()}"}
     result = {
         "metric": "chunked prefill paged attention query tokens/s (MFMA), OPT-13B shapes",
         "value": int(q_lens.sum()) / (ms_per_step * 1e-3), "unit": "query tokens/s", "n_gpus": 1,
