@@ -246,6 +246,8 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, int64_t key_t
     return fail(PA_ERR_UNSUPPORTED, "head_dim * element size (%lld bytes) must be a multiple of 16",
                 (long long)row_bytes);
   if (row_bytes > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "head_dim too large");
+  if (2 * (int64_t)num_heads * (row_bytes / 16) > 0x7fffffff)
+    return fail(PA_ERR_UNSUPPORTED, "num_heads * head_dim too large (a token's K and V exceed 2^31 16-byte chunks)");
   if (key_token_stride < (int64_t)num_heads * head_dim || value_token_stride < (int64_t)num_heads * head_dim)
     return fail(PA_ERR_INVALID_ARG, "token strides (%lld, %lld) smaller than num_heads*head_dim %lld",
                 (long long)key_token_stride, (long long)value_token_stride, (long long)num_heads * head_dim);

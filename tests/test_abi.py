@@ -85,6 +85,9 @@ def test_reshape_rejects_bad_arguments():
     assert f(FAKE, FAKE, 80, 80, FAKE, FAKE, FAKE, 3, 4, 20, 16, 10, 1, None) == 2
     assert f(None, FAKE, 512, 512, FAKE, FAKE, FAKE, 3, 4, 128, 16, 10, 1, None) == 1
     assert f(FAKE, FAKE, 512, 512, FAKE, FAKE, FAKE, 0, 4, 128, 16, 10, 1, None) == 0  # no tokens: no-op
+    # 2^20 heads of 2^16 fp32 elements: a token's K and V are 2^35 chunks of 16 B, past the
+    # kernel's 32-bit chunk index -- refused before anything is read or launched
+    assert f(FAKE, FAKE, 1 << 36, 1 << 36, FAKE, FAKE, FAKE, 1, 1 << 20, 1 << 16, 16, 10, 0, None) == 2
 
 
 def test_copy_blocks_rejects_bad_arguments():
