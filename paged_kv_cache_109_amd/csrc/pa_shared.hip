@@ -202,10 +202,14 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_prefix_ker
 
 // out[s][h] for member j of group g: the prefix chunks' partials and the
 // pass's partial of s's own positions, rescaled to a common max.  One wave
-// per (group, member, head); lanes stride over the head dimension.
+// per (group, member, head); lanes stride over the head dimension.  The
+// work is a few small reads, so their latency is what counts: each step's
+// loads are issued together (all member ids, then the chunk headers as
+// scalar loads, then the partial rows) before any of them is used.
 template <Dt T, int D>
 __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_combine_kernel(SharedArgs a) {
   constexpr int kM = kSharedMaxMembers;
+  constexpr int kU = 4;  // chunks whose loads are in flight together
   const int lane = threadIdx.x % kWave;
   const int w = blockIdx.x * kDecodeWavesPerGroup + wave_id_uniform();
   const int H = a.num_heads;
@@ -215,29 +219,59 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_combine_ke
   if (g >= a.num_groups) return;
   // Member j exists only inside the leading run of valid ids (as the prefix
   // kernel counts them).
-  for (int i = 0; i <= j; ++i) {
-    const int s = load_uniform(a.members, (int64_t)g * kM + i);
-    if (s < 0 || s >= a.num_seqs) return;
-  }
-  const int s = load_uniform(a.members, (int64_t)g * kM + j);
+  int ids[kM];
+#pragma unroll
+  for (int i = 0; i < kM; ++i) ids[i] = load_uniform(a.members, (int64_t)g * kM + i);
+#pragma unroll
+  for (int i = 0; i < kM; ++i)
+    if (i <= j && (ids[i] < 0 || ids[i] >= a.num_seqs)) return;
+  const int s = ids[j];
   const int n = clamp_len(load_uniform(a.context_lens, s), a.ctx_cap);
   const int raw = load_uniform(a.starts, s);
   const int st = raw < 0 ? 0 : min(raw & ~(kDecodeTile - 1), n);
   if (st == 0) return;  // no shared prefix for s: the pass wrote its output
   const float *sfx = a.suffix + (int64_t)s * a.suffix_row + (int64_t)h * (D + 2);
-  auto part = [&](int c) -> const float * {
-    return a.partials + ((((int64_t)g * a.chunks + c) * H + h) * kM + j) * (D + 2);
-  };
-  float M = sfx[D];
-  for (int c = 0; c < a.chunks; ++c) M = fmaxf(M, part(c)[D]);
+  const int64_t chunk_stride = (int64_t)H * kM * (D + 2);  // floats from chunk c to c+1
+  const float *part0 = a.partials + (((int64_t)g * a.chunks * H + h) * kM + j) * (D + 2);
+  const int C = a.chunks;
+  // The common max over the suffix and every chunk, then the sum.
+  const float m_sfx = load_uniform(sfx, D);
+  float M = m_sfx;
+  for (int c0 = 0; c0 < C; c0 += kU) {
+    float mc[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) mc[u] = c0 + u < C ? load_uniform(part0 + (c0 + u) * chunk_stride, D) : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) M = fmaxf(M, mc[u]);
+  }
   const float mu = (M == -INFINITY) ? 0.f : M;
-  const float ws = fast_exp2(sfx[D] - mu);  // the suffix partial is normalised: its sum is 1
+  const float ws = fast_exp2(m_sfx - mu);  // the suffix partial is normalised: its sum is 1
   float L = ws;
-  for (int c = 0; c < a.chunks; ++c) L += part(c)[D + 1] * fast_exp2(part(c)[D] - mu);
+  for (int c0 = 0; c0 < C; c0 += kU) {
+    float mc[kU], lc[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool in = c0 + u < C;
+      mc[u] = in ? load_uniform(part0 + (c0 + u) * chunk_stride, D) : -INFINITY;
+      lc[u] = in ? load_uniform(part0 + (c0 + u) * chunk_stride, D + 1) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) L += lc[u] * fast_exp2(mc[u] - mu);
+  }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   for (int d = lane; d < D; d += kWave) {
     float A = sfx[d] * ws;
-    for (int c = 0; c < a.chunks; ++c) A += part(c)[d] * fast_exp2(part(c)[D] - mu);
+    for (int c0 = 0; c0 < C; c0 += kU) {
+      float v[kU], mc[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const bool in = c0 + u < C;
+        v[u] = in ? part0[(c0 + u) * chunk_stride + d] : 0.f;
+        mc[u] = in ? load_uniform(part0 + (c0 + u) * chunk_stride, D) : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) A += v[u] * fast_exp2(mc[u] - mu);
+    }
     const float o = A * inv;
     const int64_t idx = ((int64_t)s * H + h) * D + d;
     if constexpr (T == Dt::F32) reinterpret_cast<float *>(a.out)[idx] = o;
