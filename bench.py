@@ -51,6 +51,9 @@ def parse():
                     help="worker waves the tile stream is cut among (0: as many as the GPU holds)")
     ap.add_argument("--dtype", default=None, choices=["f16", "bf16", "f32"],
                     help="element type of the decode workloads (default: the workload's own, fp16)")
+    ap.add_argument("--num-seqs", type=int, default=None,
+                    help="batch size of the opt13b_b64 (uniform lengths) or large_batch_b256 (lognormal "
+                         "lengths) decode workload (default: 64 and 256)")
     ap.add_argument("--block-size", type=int, default=16,
                     help="tokens per KV block for the decode workloads (4, 8, 16, 32 or 64)")
     ap.add_argument("--graph", action="store_true",
@@ -211,6 +214,11 @@ def main():
         return bench_prefill(args)
     t0 = time.time()
     extra = {"dtype": args.dtype} if args.dtype else {}
+    if args.num_seqs is not None:
+        if args.workload not in ("opt13b_b64", "large_batch_b256") or args.num_seqs < 1:
+            print("--num-seqs applies to the opt13b_b64 and large_batch_b256 workloads (>= 1)", file=sys.stderr)
+            sys.exit(2)
+        extra["num_seqs"] = args.num_seqs
     case = {"opt13b_b64": W.opt13b_b64, "large_batch_b256": W.large_batch_b256,
             "parallel_sampling": W.parallel_sampling}[args.workload](block_size=args.block_size, **extra)
     print(f"[bench] workload {case.name} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)

@@ -309,28 +309,29 @@ def _suffix(block_size: int) -> str:
     return "" if block_size == OPT13B["block_size"] else f"_B{block_size}"
 
 
-def opt13b_b64(seed: int = 0, dtype: str = "f16", block_size: int = 16) -> PagedCase:
-    """OPT-13B layer: batch 64, 40 heads x 128, B=16 (or block_size),
-    lengths uniform in [1, 2048]; the pool holds exactly the needed blocks,
-    placed by a random permutation; one new token per sequence at position
-    ctx-1."""
+def opt13b_b64(seed: int = 0, dtype: str = "f16", block_size: int = 16, num_seqs: int = 64) -> PagedCase:
+    """OPT-13B layer: batch 64 (or num_seqs), 40 heads x 128, B=16 (or
+    block_size), lengths uniform in [1, 2048]; the pool holds exactly the
+    needed blocks, placed by a random permutation; one new token per
+    sequence at position ctx-1."""
     return make_decode_case(
-        64, dtype=dtype, context_lens=lambda r, n: r.integers(1, 2049, size=n), seed=seed,
+        num_seqs, dtype=dtype, context_lens=lambda r, n: r.integers(1, 2049, size=n), seed=seed,
         max_blocks_per_seq=-(-2048 // block_size), new_tokens=True,
-        name="opt13b_b64_" + dtype + _suffix(block_size), **_shape(block_size))
+        name=f"opt13b_b{num_seqs}_" + dtype + _suffix(block_size), **_shape(block_size))
 
 
 def _lognormal_ctx(r, n):
     return np.clip(np.rint(r.lognormal(mean=np.log(300.0), sigma=1.0, size=n)), 8, 2048).astype(np.int32)
 
 
-def large_batch_b256(seed: int = 0, dtype: str = "f16", block_size: int = 16) -> PagedCase:
-    """Batch 256 with lognormal lengths (median 300, sigma 1, clipped to
-    [8, 2048]), random placement; one new token per sequence at ctx-1."""
+def large_batch_b256(seed: int = 0, dtype: str = "f16", block_size: int = 16, num_seqs: int = 256) -> PagedCase:
+    """Batch 256 (or num_seqs) with lognormal lengths (median 300, sigma 1,
+    clipped to [8, 2048]), random placement; one new token per sequence at
+    ctx-1."""
     return make_decode_case(
-        256, dtype=dtype, context_lens=_lognormal_ctx, seed=seed,
+        num_seqs, dtype=dtype, context_lens=_lognormal_ctx, seed=seed,
         max_blocks_per_seq=-(-2048 // block_size), new_tokens=True,
-        name="large_batch_b256_" + dtype + _suffix(block_size), **_shape(block_size))
+        name=f"large_batch_b{num_seqs}_" + dtype + _suffix(block_size), **_shape(block_size))
 
 
 def parallel_sampling(seed: int = 0, prompt_len: int = 512, groups: int = 32, samples: int = 6,
