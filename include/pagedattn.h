@@ -175,6 +175,60 @@ pa_status pa_paged_attention_decode(void *out, const void *q, const void *k_cach
                                     float scale, pa_dtype dtype, int32_t split_workers,
                                     void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * pa_paged_attention_decode_append -- the decode step's cache write and its
+ * attention in one pass.  A decode step first stores the new token's K and V
+ * in its slot, then attends over a context that includes it ("KV 캐시 관리와
+ * PagedAttention", section on attention over scattered KV).  The pages fuse
+ * the write's steps into one kernel to save launches (review section 5.1,
+ * item 1; notes section 4.1); this call goes one launch further: the
+ * partition pass reads the newest token from key/value and writes it into
+ * the cache itself.
+ *
+ * For each sequence s with n = context_lens[s] >= 1 (clipped to
+ * max_context_len as in pa_paged_attention_decode), key[s] and value[s]
+ * ([num_heads][head_dim] each) are the K and V of position n - 1.  The call
+ * leaves the caches and `out` byte for byte as
+ *     pa_reshape_and_cache(key, value, ..., slot_mapping) with
+ *         slot_mapping[s] = block_tables[s][(n-1)/B] * B + (n-1) % B,
+ *     then pa_paged_attention_decode(...)
+ * would.  A sequence with n = 0 writes nothing; a table entry for position
+ * n - 1 outside [0, num_blocks) is neither read nor written (as both calls
+ * skip it).
+ *
+ *  key, value        device, sequence s's rows at key + s*key_seq_stride
+ *                    (elements; >= num_heads*head_dim, whole 16-byte units),
+ *                    heads contiguous; a fused QKV tensor's slices work.
+ *  k_cache, v_cache  written at each sequence's slot of position n - 1.
+ *  others            as for pa_paged_attention_decode (same workspace size).
+ *
+ * Beyond pa_paged_attention_decode's preconditions: the block holding
+ * position n - 1 of a sequence is not read by another sequence of the batch
+ * (true of any copy-on-write table: a block written to has one owner), and
+ * key/value do not overlap the caches.  Under PA_DEBUG_VALIDATE the table
+ * and length checks of pa_paged_attention_decode apply.
+ */
+pa_status pa_paged_attention_decode_append(void *out, const void *q, const void *key,
+                                           const void *value, int64_t key_seq_stride,
+                                           int64_t value_seq_stride, void *k_cache, void *v_cache,
+                                           const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t *context_lens, int32_t max_context_len,
+                                           int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                           int32_t block_size, int64_t num_blocks, float scale,
+                                           pa_dtype dtype, int32_t split_workers, void *workspace,
+                                           size_t workspace_bytes, void *stream);
+
+/* The partition pass of pa_paged_attention_decode_append alone (same
+ * arguments), cache write included; pa_paged_attention_decode_reduce then
+ * finishes it exactly as it finishes pa_paged_attention_decode_partitions. */
+pa_status pa_paged_attention_decode_append_partitions(
+    void *out, const void *q, const void *key, const void *value, int64_t key_seq_stride,
+    int64_t value_seq_stride, void *k_cache, void *v_cache, const int32_t *block_tables,
+    int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+    int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+    float scale, pa_dtype dtype, int32_t split_workers, void *workspace, size_t workspace_bytes,
+    void *stream);
+
 /* The partition pass alone (same arguments).  Writes `out` for every pair
  * that one worker wave finished and the workspace (plan and partial
  * results) for the others. */

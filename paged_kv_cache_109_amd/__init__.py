@@ -24,6 +24,8 @@ from ._binding import (  # noqa: F401
     decode_default_workers,
     decode_workspace_bytes,
     paged_attention_decode,
+    paged_attention_decode_append,
+    paged_attention_decode_append_partitions,
     paged_attention_decode_partitions,
     paged_attention_decode_reduce,
     paged_attention_decode_shared,

@@ -37,6 +37,12 @@ _SIGS = {
         [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, i32, P, sz, P], ctypes.c_int),
     "pa_paged_attention_decode_partitions": (
         [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, i32, P, sz, P], ctypes.c_int),
+    "pa_paged_attention_decode_append": (
+        [P, P, P, P, i64, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, i32, P, sz, P],
+        ctypes.c_int),
+    "pa_paged_attention_decode_append_partitions": (
+        [P, P, P, P, i64, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, i32, P, sz, P],
+        ctypes.c_int),
     "pa_paged_attention_decode_reduce": (
         [P, P, i32, i32, i32, i32, i32, i32, ctypes.c_int, i32, P, sz, P], ctypes.c_int),
     "pa_copy_blocks": ([P, P, i32, P, i64, i64, i64, P], ctypes.c_int),
@@ -186,6 +192,46 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
                                                         max_context_len, scale, split_workers, workspace,
                                                         stream)), "paged_attention_decode")
     return out
+
+
+def _append_args(out, q, key, value, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                 split_workers, workspace, stream):
+    args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                        split_workers, workspace, stream)
+    S, H, D = int(q.shape[0]), int(k_cache.shape[1]), int(k_cache.shape[3])
+    for name, t in (("key", key), ("value", value)):
+        if t.shape != (S, H, D) or t.dtype != k_cache.dtype:
+            raise ValueError(f"{name} must be [{S}, {H}, {D}] {k_cache.dtype}")
+        if S and (t.stride(2) != 1 or t.stride(1) != D):
+            raise ValueError(f"{name}: heads and head_dim must be contiguous within a sequence's row")
+    return (args[0], args[1], _dev(key, "key"), _dev(value, "value"), key.stride(0), value.stride(0)) + args[2:]
+
+
+def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                                  k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                  context_lens: torch.Tensor, max_context_len: int, scale: float,
+                                  workspace: Optional[torch.Tensor] = None, split_workers: int = 0,
+                                  stream=None) -> torch.Tensor:
+    """The decode step's cache write and attention in one pass: key[s] /
+    value[s] ([S, H, D], sequence-strided views allowed) are the K/V of
+    position context_lens[s] - 1, written into its cache slot and attended
+    over. Same caches and output bytes as reshape_and_cache at those slots
+    followed by paged_attention_decode."""
+    if workspace is None:
+        workspace = alloc_decode_workspace(q.shape[0], k_cache.shape[1], k_cache.shape[3], max_context_len,
+                                           k_cache.shape[2], split_workers, device=q.device)
+    _check(_lib.pa_paged_attention_decode_append(*_append_args(
+        out, q, key, value, k_cache, v_cache, block_tables, context_lens, max_context_len, scale, split_workers,
+        workspace, stream)), "paged_attention_decode_append")
+    return out
+
+
+def paged_attention_decode_append_partitions(out, q, key, value, k_cache, v_cache, block_tables, context_lens,
+                                             max_context_len, scale, workspace=None, split_workers=0,
+                                             stream=None) -> None:
+    _check(_lib.pa_paged_attention_decode_append_partitions(*_append_args(
+        out, q, key, value, k_cache, v_cache, block_tables, context_lens, max_context_len, scale, split_workers,
+        workspace, stream)), "paged_attention_decode_append_partitions")
 
 
 MAX_GROUP_MEMBERS = 8

@@ -158,6 +158,10 @@ pa::DecodeArgs decode_args(void *out, const void *q, const void *k_cache, const 
   a.starts = nullptr;
   a.suffix_out = nullptr;
   a.suffix_row = num_heads * (head_dim + 2);
+  a.new_key = nullptr;
+  a.new_value = nullptr;
+  a.new_key_stride = 0;
+  a.new_value_stride = 0;
   return a;
 }
 
@@ -283,12 +287,18 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t he
   return geometry(head_dim, max_context_len, -1, block_size, worker_bound(split_workers)).ws_bytes;
 }
 
+// The newest token's rows for the fused append (decode_impl's `app`).
+struct AppendRows {
+  const void *key, *value;
+  int64_t key_stride, value_stride;  // elements between sequences' rows
+};
+
 static pa_status decode_impl(bool run_parts, bool run_reduce, void *out, const void *q, const void *k_cache,
                              const void *v_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
                              const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
                              int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                              float scale, pa_dtype dtype, int32_t split_workers, void *workspace,
-                             size_t workspace_bytes, void *stream) {
+                             size_t workspace_bytes, void *stream, const AppendRows *app = nullptr) {
   pa_status st = check_decode_common(k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                                      max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks,
                                      dtype, split_workers);
@@ -296,13 +306,30 @@ static pa_status decode_impl(bool run_parts, bool run_reduce, void *out, const v
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
   if (num_seqs > 0 && (!out || !q)) return fail(PA_ERR_INVALID_ARG, "null out or q pointer");
   if (!aligned16(out) || !aligned16(q)) return fail(PA_ERR_INVALID_ARG, "out and q must be 16-byte aligned");
+  if (app) {
+    const int64_t row = (int64_t)num_heads * head_dim;
+    if (num_seqs > 0 && (!app->key || !app->value)) return fail(PA_ERR_INVALID_ARG, "null key or value pointer");
+    if (!aligned16(app->key) || !aligned16(app->value))
+      return fail(PA_ERR_INVALID_ARG, "key and value must be 16-byte aligned");
+    if (app->key_stride < row || app->value_stride < row)
+      return fail(PA_ERR_INVALID_ARG, "sequence strides (%lld, %lld) smaller than num_heads*head_dim %lld",
+                  (long long)app->key_stride, (long long)app->value_stride, (long long)row);
+    if ((app->key_stride * elt_bytes(dtype)) % 16 != 0 || (app->value_stride * elt_bytes(dtype)) % 16 != 0)
+      return fail(PA_ERR_INVALID_ARG, "sequence strides must be whole 16-byte units");
+  }
   if (num_seqs == 0) return ok();
   const DecodeGeometry g = geometry(head_dim, max_context_len, max_blocks_per_seq, block_size,
                                     decode_workers(dtype, head_dim, block_size, split_workers));
   st = check_workspace(g, workspace, workspace_bytes);
   if (st != PA_OK) return st;
-  const pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
-                                       num_seqs, num_heads, head_dim, dtype, num_blocks, scale, g, workspace);
+  pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                                 num_seqs, num_heads, head_dim, dtype, num_blocks, scale, g, workspace);
+  if (app) {
+    a.new_key = app->key;
+    a.new_value = app->value;
+    a.new_key_stride = app->key_stride * elt_bytes(dtype);
+    a.new_value_stride = app->value_stride * elt_bytes(dtype);
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (run_parts && pa::debug_validate()) {
     st = pa::validate_decode(block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs, block_size,
@@ -329,6 +356,31 @@ pa_status pa_paged_attention_decode(void *out, const void *q, const void *k_cach
   return decode_impl(true, true, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                      max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks, scale, dtype,
                      split_workers, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_paged_attention_decode_append(void *out, const void *q, const void *key, const void *value,
+                                           int64_t key_seq_stride, int64_t value_seq_stride, void *k_cache,
+                                           void *v_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                                           int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                           int64_t num_blocks, float scale, pa_dtype dtype, int32_t split_workers,
+                                           void *workspace, size_t workspace_bytes, void *stream) {
+  const AppendRows app{key, value, key_seq_stride, value_seq_stride};
+  return decode_impl(true, true, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks, scale, dtype,
+                     split_workers, workspace, workspace_bytes, stream, &app);
+}
+
+pa_status pa_paged_attention_decode_append_partitions(
+    void *out, const void *q, const void *key, const void *value, int64_t key_seq_stride, int64_t value_seq_stride,
+    void *k_cache, void *v_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+    const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype, int32_t split_workers, void *workspace,
+    size_t workspace_bytes, void *stream) {
+  const AppendRows app{key, value, key_seq_stride, value_seq_stride};
+  return decode_impl(true, false, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks, scale, dtype,
+                     split_workers, workspace, workspace_bytes, stream, &app);
 }
 
 pa_status pa_paged_attention_decode_partitions(void *out, const void *q, const void *k_cache, const void *v_cache,

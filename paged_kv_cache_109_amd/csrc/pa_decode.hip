@@ -338,7 +338,12 @@ __device__ __forceinline__ void merge_fragments(const DecodeArgs &a, uint32_t wa
   }
 }
 
-template <Dt T, int D, int B>
+// kAppend: each sequence's newest token (position n - 1) comes from
+// a.new_key / a.new_value instead of the cache, and the wave that consumes
+// the tile holding it writes those rows into the cache.  Exactly one wave
+// consumes that tile of a (sequence, head) and it reads the token from the
+// new rows, so no wave of the launch reads the cache row being written.
+template <Dt T, int D, int B, bool kAppend>
 __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_kernel(DecodeArgs a) {
   using R = RowShape<T, D>;
   const int lane = threadIdx.x % kWave;
@@ -391,6 +396,8 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_
     // the whole tile (base < n always holds for a live tile).
     int32_t tile_phys = -1;
     if constexpr (B >= kDecodeTile) tile_phys = live ? entry(ic.s, base / B) : -1;
+    // Append: the last tile of a sequence holds position n - 1.
+    [[maybe_unused]] const bool tail = kAppend && live && base + kDecodeTile >= ic.n;
     okm = 0;
 #pragma unroll
     for (int i = 0; i < R::kNI; ++i) {
@@ -411,8 +418,19 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_
       const bool ok = live && (pos < ic.n) && (phys >= 0);
       const int64_t off =
           ok ? (int64_t)phys * block_stride + head_off + (int64_t)(pos % B) * R::kRowBytes : (int64_t)col * 16;
-      kf[i] = load16(kbase + off);
-      vf[i] = load16(vbase + off);
+      if constexpr (kAppend) {
+        const char *kp = kbase + off, *vp = vbase + off;
+        if (tail && ok && pos == ic.n - 1) {
+          kp = reinterpret_cast<const char *>(a.new_key) + (int64_t)s * a.new_key_stride + h * R::kRowBytes + col * 16;
+          vp = reinterpret_cast<const char *>(a.new_value) + (int64_t)s * a.new_value_stride + h * R::kRowBytes +
+               col * 16;
+        }
+        kf[i] = load16(kp);
+        vf[i] = load16(vp);
+      } else {
+        kf[i] = load16(kbase + off);
+        vf[i] = load16(vbase + off);
+      }
       okm |= ok ? (1u << i) : 0u;
     }
   };
@@ -474,6 +492,32 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_
   // Fold one tile into the running state of the pair under the consume cursor.
   constexpr uint32_t kAll = (1u << R::kNI) - 1u;
   auto consume = [&](const uint4 *kf, uint4 *vf, const uint4 &qslot, uint32_t okm) {
+    // Append: the last tile of a pair holds position n - 1, whose rows were
+    // just loaded from the new rows; write them into its cache slot.  A
+    // token outside the pool is neither read nor written.
+    if constexpr (kAppend) {
+      if (cc.t + 1 == cc.nt) {
+        const int p = cc.n - 1;
+        const int r = p - (cc.st + cc.t * kDecodeTile);  // its row within the tile
+        const int32_t phys = entry(cc.s, p / B);
+        // The load holding row r, picked with masks: a select of the slot's
+        // registers would become one load at a computed index, which puts
+        // the whole ring in scratch memory.
+        uint4 kn = make_uint4(0, 0, 0, 0), vn = kn;
+#pragma unroll
+        for (int i = 0; i < R::kNI; ++i) {
+          const uint32_t m = i == r / R::kGroups ? ~0u : 0u;
+          kn.x |= kf[i].x & m, kn.y |= kf[i].y & m, kn.z |= kf[i].z & m, kn.w |= kf[i].w & m;
+          vn.x |= vf[i].x & m, vn.y |= vf[i].y & m, vn.z |= vf[i].z & m, vn.w |= vf[i].w & m;
+        }
+        if (phys >= 0 && grp == r % R::kGroups) {
+          const int64_t off =
+              (int64_t)phys * block_stride + ((int64_t)cc.h * B + p % B) * R::kRowBytes + col * 16;
+          *reinterpret_cast<uint4 *>(const_cast<char *>(kbase) + off) = kn;
+          *reinterpret_cast<uint4 *>(const_cast<char *>(vbase) + off) = vn;
+        }
+      }
+    }
     if (cc.t == 0 || cc.g == g0) {
       qcur = qslot;
       m_run = -INFINITY;
@@ -566,11 +610,15 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_reduce_ker
 
 // ------------------------------------------------------------------ dispatch
 
+// Both variants launch this many workers per CU (the plain kernel's
+// occupancy), so the workspace layout and the reduce pass do not depend on
+// the variant; where the append variant holds fewer waves at once, the
+// extra workers simply start later.
 template <Dt T, int D, int B>
 static int waves_per_cu() {
   static const int v = [] {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partition_kernel<T, D, B>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partition_kernel<T, D, B, false>,
                                                      kDecodeWavesPerGroup * kWave, 0) != hipSuccess ||
         nb < 1)
       nb = 1;
@@ -587,8 +635,12 @@ static hipError_t launch_part(const DecodeArgs &a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   const unsigned groups = (unsigned)((a.workers + kDecodeWavesPerGroup - 1) / kDecodeWavesPerGroup);
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, B>), dim3(groups), dim3(kDecodeWavesPerGroup * kWave), 0, st,
-                     a);
+  if (a.new_key)
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, B, true>), dim3(groups), dim3(kDecodeWavesPerGroup * kWave), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, B, false>), dim3(groups), dim3(kDecodeWavesPerGroup * kWave), 0,
+                       st, a);
   return hipGetLastError();
 }
 

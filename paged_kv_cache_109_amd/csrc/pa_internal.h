@@ -41,6 +41,14 @@ struct DecodeArgs {
   const int32_t *starts;
   float *suffix_out;
   int32_t suffix_row;  // floats of suffix_out per sequence: num_heads * (head_dim + 2)
+  // Fused append only (both null otherwise): the K and V rows ([H][D]) of
+  // each sequence's newest token, position n - 1, new_*_stride bytes apart.
+  // The pass reads that position from them instead of the cache and writes
+  // them into the cache (k_cache / v_cache are then writable).
+  const void *new_key;
+  const void *new_value;
+  int64_t new_key_stride;
+  int64_t new_value_stride;
 };
 
 // 32-bit words before the per-worker starts in the plan.
@@ -55,6 +63,7 @@ constexpr int kMaxWavesPerCu = 32;
 // Resident worker waves per CU of the decode instantiation (0 if unsupported).
 int decode_waves_per_cu(int dtype, int head_dim, int block_size);
 bool decode_supported(int dtype, int head_dim, int block_size);
+// Launches the fused-append instantiation when a.new_key is set.
 hipError_t launch_decode_partitions(const DecodeArgs &a, int dtype, int head_dim, int block_size,
                                     hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream);

@@ -68,6 +68,27 @@ def test_decode_rejects_bad_arguments(over, status):
     assert B._lib.pa_last_error()
 
 
+def decode_append(partitions=False, **over):
+    a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, ks=512, vs=512, k=FAKE, v=FAKE, bt=FAKE, M=8, ctx=FAKE,
+             max_ctx=100, S=2, H=4, D=128, Bs=16, N=64, scale=0.1, dt=1, part=0, ws=None, ws_bytes=0, stream=None)
+    a.update(over)
+    fn = B._lib.pa_paged_attention_decode_append_partitions if partitions else B._lib.pa_paged_attention_decode_append
+    return fn(a["out"], a["q"], a["key"], a["value"], a["ks"], a["vs"], a["k"], a["v"], a["bt"], a["M"], a["ctx"],
+              a["max_ctx"], a["S"], a["H"], a["D"], a["Bs"], a["N"], a["scale"], a["dt"], a["part"], a["ws"],
+              a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("partitions", [False, True])
+@pytest.mark.parametrize("over,status", [
+    (dict(dt=7), 1), (dict(D=96), 2), (dict(k=None), 1), (dict(scale=float("inf")), 1),
+    (dict(key=None), 1), (dict(value=FAKE + 8), 1), (dict(ks=511), 1), (dict(vs=4), 1), (dict(ks=516), 1),
+    (dict(max_ctx=2048, M=128), 3),
+])
+def test_decode_append_rejects_bad_arguments(over, status, partitions):
+    assert decode_append(partitions, **over) == status
+    assert B._lib.pa_last_error()
+
+
 def test_workspace_sizing():
     def ws(workers, D=128):
         return -(-(4 + 2 * workers) * 4 // 256) * 256 + workers * 2 * (D + 2) * 4
