@@ -58,6 +58,9 @@ def parse():
                     help="tokens per KV block for the decode workloads (4, 8, 16, 32 or 64)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the step captured as a HIP graph instead of eager launches")
+    ap.add_argument("--step", default="separate", choices=["fused", "separate"],
+                    help="decode workloads with one new token per sequence: write it inside the partition pass "
+                         "(fused, paged_attention_decode_append) or with reshape_and_cache first (separate)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU oracle on the batch until this much time has passed (at least 3 runs)")
@@ -243,6 +246,10 @@ def main():
     copies = case.block_mapping is not None
     if copies:
         mapping = to_dev(case.block_mapping)
+    # The fused step needs exactly one new token per sequence, at its last
+    # position, and nothing written before it.
+    fused = (args.step == "fused" and writes and not copies and len(case.new_seq) == S
+             and (case.new_seq == np.arange(S)).all() and (case.new_pos == case.context_lens - 1).all())
     out = torch.empty_like(q)
     max_ctx = case.max_context_len
     workers = args.split_workers
@@ -260,12 +267,17 @@ def main():
             ev[0].record(stream)
         if copies:
             pa.copy_blocks([k_cache], [v_cache], mapping)
-        if writes:
+        if writes and not fused:
             pa.reshape_and_cache(new_k, new_v, k_cache, v_cache, slots)
         if ev is not None:
             ev[1].record(stream)
-        pa.paged_attention_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, max_ctx,
-                                             case.scale, workspace=ws, split_workers=workers)
+        if fused:
+            pa.paged_attention_decode_append_partitions(out, q, new_k, new_v, k_cache, v_cache, block_tables,
+                                                        context_lens, max_ctx, case.scale, workspace=ws,
+                                                        split_workers=workers)
+        else:
+            pa.paged_attention_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, max_ctx,
+                                                 case.scale, workspace=ws, split_workers=workers)
         if ev is not None:
             ev[2].record(stream)
         pa.paged_attention_decode_reduce(out, context_lens, max_ctx, case.max_blocks_per_seq, H, D, B,
@@ -295,19 +307,20 @@ def main():
     kv_bytes = W.logical_kv_bytes(case.context_lens, H, D, elt)
     nblocks = int(sum(W.blocks_needed(n, B) for n in case.context_lens))
     # Algorithmic bytes of one partition-pass launch: every valid token's K and
-    # V row once, q in, the output out, the table entries and lengths.
-    alg_bytes = kv_bytes + 2 * S * H * D * elt + 4 * nblocks + 4 * S
+    # V row once, q in, the output out, the table entries and lengths; fused,
+    # also the new token's K and V rows written into the cache.
+    alg_bytes = kv_bytes + 2 * S * H * D * elt + 4 * nblocks + 4 * S + (2 * S * H * D * elt if fused else 0)
     achieved = alg_bytes / part_avg_s / 1e9
     tokens_per_s = S / (ms_per_step * 1e-3)
     # Counter summaries are committed for the 16-token-block workloads only.
-    traffic = (committed_traffic("decode_partition_" + case.name.rsplit("_", 1)[0])
+    traffic = (committed_traffic("decode_partition_" + ("append_" if fused else "") + case.name.rsplit("_", 1)[0])
                if B == 16 and case.dtype == "f16" else None)
 
     # The other kernels of the step, each timed by its own events: algorithmic
     # bytes are what the call must read plus what it must write.
     components = {"decode_reduce_kernel": {"avg_us": red_avg_s * 1e6}}
     row = H * D * elt
-    if writes:
+    if writes and not fused:
         T = int(case.new_key.shape[0])
         b = 2 * (2 * T * row) + 8 * T
         components["reshape_and_cache_kernel"] = {"tokens": T, "alg_bytes": b, "avg_us": pre_avg_s * 1e6,
@@ -431,12 +444,14 @@ def main():
                    "split_workers": workers or pa.decode_default_workers(tdt, D, B), "pool_replicas": args.replicas,
                    "step_launch": launch,
                    "step": ("copy_blocks(CoW pairs) + " if copies else "")
-                   + ("reshape_and_cache(new tokens) + " if writes else "") + "decode partitions + decode reduce"},
+                   + ("decode partitions with the new tokens' cache write fused in + decode reduce" if fused else
+                      ("reshape_and_cache(new tokens) + " if writes else "") + "decode partitions + decode reduce")},
         "effective_kv_gbps": kv_bytes / (ms_per_step * 1e-3) / 1e9,
         "pct_hbm_peak": kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "stream_read": stream_read,
         "pct_of_stream_read": kv_bytes / (ms_per_step * 1e-3) / 1e9 / stream_read["gbps"],
-        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel" + (" (append)" if fused else ""),
+                     "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "alg_bytes_per_launch": alg_bytes, "avg_launch_us": part_avg_s * 1e6,
                      **launch_stats(part_ms), "frac_of_stream_read": achieved / stream_read["gbps"]},
