@@ -101,3 +101,43 @@ def test_prefill_step_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
+
+
+def test_decode_append_step_graph_replays_match_eager():
+    c = W.make_decode_case(6, 8, 128, 16, "bf16", [1, 17, 640, 2048, 33, 250], seed=13, new_tokens=True,
+                           max_blocks_per_seq=128)
+    dc = DeviceCase(c)
+    nk, nv = dev(c.new_key, c.dtype), dev(c.new_value, c.dtype)
+    slots = oracle.slots(c.block_tables, c.new_seq, c.new_pos, c.block_size)
+    ws = pa.alloc_decode_workspace(6, 8, 128, c.max_context_len, 16)
+    out = torch.empty_like(dc.q)
+
+    def step():
+        pa.paged_attention_decode_append(out, dc.q, nk, nv, dc.k_cache, dc.v_cache, dc.block_tables,
+                                         dc.context_lens, c.max_context_len, c.scale, workspace=ws)
+
+    say("  append step: eager")
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    oracle.reshape_and_cache(c.k_cache, c.v_cache, c.new_key, c.new_value, slots, c.dtype)
+    check_attention(eager, oracle.decode(c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.scale,
+                                         c.dtype), c.dtype, "eager append step")
+    blk = torch.from_numpy(slots // 16).cuda()
+    off = torch.from_numpy(slots % 16).cuda()
+    g = capture(step)
+    for r in range(4):
+        # Eager work between replays: clobber the output and the rows the
+        # step writes (it never reads them), then run another decode.
+        out.fill_(float("nan"))
+        dc.k_cache[blk, :, off] = float("nan")
+        dc.v_cache[blk, :, off] = float("nan")
+        pa.paged_attention_decode(torch.empty_like(out), dc.q, dc.k_cache, dc.v_cache, dc.block_tables,
+                                  dc.context_lens, c.max_context_len, c.scale, workspace=ws, split_workers=5)
+        torch.cuda.synchronize()
+        say(f"  append step: replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
+        assert torch.equal(dc.k_cache[blk, :, off].view(torch.int16), nk.view(torch.int16))
+        assert torch.equal(dc.v_cache[blk, :, off].view(torch.int16), nv.view(torch.int16))
