@@ -306,34 +306,80 @@ __device__ __forceinline__ uint32_t first_worker(uint32_t pair_start, uint32_t t
   return (uint32_t)((((uint64_t)pair_start + 1) * G + total - 1) / total) - 1;
 }
 
+// Fragments a merge reads in one batch (a pair usually spans a few
+// workers); longer runs take the loop below.
+constexpr uint32_t kMergeBatch = 8;
+
 // Merge the fragments workers wa..wb left for pair (s, h) and write its
 // output row: wa's is in its back slot (1), every later worker's in its front
-// slot (0).  One wave; lanes stride over the head dimension.
+// slot (0).  One wave; lanes stride over the head dimension.  The sums run
+// over the fragments in order either way, so both paths give the same bits.
 template <Dt T, int D>
 __device__ __forceinline__ void merge_fragments(const DecodeArgs &a, uint32_t wa, uint32_t wb, int s, int h) {
   const int lane = threadIdx.x % kWave;
   auto frag = [&](uint32_t v) -> const float * {
     return a.frags + ((int64_t)v * 2 + (v == wa ? 1 : 0)) * (D + 2);
   };
-  float M = -INFINITY;
-  for (uint32_t v = wa; v <= wb; ++v) M = fmaxf(M, frag(v)[D]);
-  const float mu = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f;
-  for (uint32_t v = wa; v <= wb; ++v) L += frag(v)[D + 1] * fast_exp2(frag(v)[D] - mu);
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  constexpr int kPer = (D + kWave - 1) / kWave;  // head dimensions per lane
+  const uint32_t cnt = wb - wa + 1;
   const int n = clip_ctx(a.context_lens[s], a.ctx_cap);
+  float M = -INFINITY, L = 0.f, A[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) A[j] = 0.f;
+  if (cnt <= kMergeBatch) {
+    // Every load first, so they are in flight together: lane v reads
+    // fragment wa+v's max and sum, and every lane its dimensions of each
+    // fragment (indices past wb repeat wb's and are not summed).
+    const float *fl = frag(wa + min((uint32_t)lane, cnt - 1));
+    const float mv = fl[D], lv = fl[D + 1];
+    float x[kMergeBatch][kPer];
+#pragma unroll
+    for (uint32_t v = 0; v < kMergeBatch; ++v) {
+      const float *f = frag(wa + min(v, cnt - 1));
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) x[v][j] = (lane + kWave * j < D) ? f[lane + kWave * j] : 0.f;
+    }
+#pragma unroll
+    for (uint32_t v = 0; v < kMergeBatch; ++v)
+      if (v < cnt) M = fmaxf(M, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mv), v)));
+    const float mu = (M == -INFINITY) ? 0.f : M;
+#pragma unroll
+    for (uint32_t v = 0; v < kMergeBatch; ++v) {
+      if (v < cnt) {
+        const float e = fast_exp2(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(mv), v)) - mu);
+        L += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), v)) * e;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) A[j] += x[v][j] * e;
+      }
+    }
+    M = mu;
+  } else {
+    for (uint32_t v = wa; v <= wb; ++v) M = fmaxf(M, frag(v)[D]);
+    const float mu = (M == -INFINITY) ? 0.f : M;
+    for (uint32_t v = wa; v <= wb; ++v) L += frag(v)[D + 1] * fast_exp2(frag(v)[D] - mu);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int d = lane + kWave * j;
+      if (d < D)
+        for (uint32_t v = wa; v <= wb; ++v) A[j] += frag(v)[d] * fast_exp2(frag(v)[D] - mu);
+    }
+    M = mu;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
   float *part = nullptr;
   if (a.starts && to_partial(a, start_of(a.starts[s], n)))
     part = a.suffix_out + (int64_t)s * a.suffix_row + (int64_t)h * (D + 2);
   const int64_t out_row = ((int64_t)s * a.num_heads + h) * D;
-  for (int d = lane; d < D; d += kWave) {
-    float A = 0.f;
-    for (uint32_t v = wa; v <= wb; ++v) A += frag(v)[d] * fast_exp2(frag(v)[D] - mu);
-    if (part) part[d] = A * inv;
-    else store_out_elem<T, D>(a.out, out_row + d, A * inv);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int d = lane + kWave * j;
+    if (d < D) {
+      if (part) part[d] = A[j] * inv;
+      else store_out_elem<T, D>(a.out, out_row + d, A[j] * inv);
+    }
   }
   if (part && lane == 0) {
-    part[D] = L > 0.f ? mu + __builtin_amdgcn_logf(L) : -INFINITY;
+    part[D] = L > 0.f ? M + __builtin_amdgcn_logf(L) : -INFINITY;
     part[D + 1] = 0.f;
   }
 }
