@@ -191,3 +191,30 @@ def test_prefill_chunk(validate):
     refused(lambda: call(sentinel, bt=bad), "block_tables[0][2]")
     torch.cuda.synchronize()
     assert bool((sentinel == 7.0).all())
+
+
+def test_decode_append(validate):
+    c, q, k, v, bt, ctx = decode_case()
+    rng = np.random.default_rng(9)
+    nk = dev(W.normal_cast(rng, (4, 2, 64), "f16"))
+    nv = dev(W.normal_cast(rng, (4, 2, 64), "f16"))
+    k2, v2 = k.clone(), v.clone()
+    out = pa.paged_attention_decode_append(torch.empty_like(q), q, nk, nv, k2, v2, bt, ctx, 64, c.scale)
+    torch.cuda.synchronize()
+    plain, k3, v3 = torch.empty_like(q), k.clone(), v.clone()
+    with pytest.MonkeyPatch.context() as m:
+        m.delenv("PA_DEBUG_VALIDATE")
+        pa.paged_attention_decode_append(plain, q, nk, nv, k3, v3, bt, ctx, 64, c.scale)
+        torch.cuda.synchronize()
+    assert torch.equal(out, plain) and torch.equal(k2, k3) and torch.equal(v2, v3)
+
+    # A refused call writes neither the output nor the caches.
+    sentinel, k4, v4 = torch.full_like(q, 7.0), k.clone(), v.clone()
+    bad = bt.clone()
+    bad[1, 1] = c.k_cache.shape[0]  # position 16 of a 17-token context: the newest token's block
+    refused(lambda: pa.paged_attention_decode_append(sentinel, q, nk, nv, k4, v4, bad, ctx, 64, c.scale),
+            "block_tables[1][1]")
+    refused(lambda: pa.paged_attention_decode_append(sentinel, q, nk, nv, k4, v4, bt, ctx, 63, c.scale),
+            "context_lens[3] = 64")
+    torch.cuda.synchronize()
+    assert bool((sentinel == 7.0).all()) and torch.equal(k4, k) and torch.equal(v4, v)
