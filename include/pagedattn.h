@@ -367,6 +367,43 @@ pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32
                                            void *stream);
 
 /*
+ * pa_paged_attention_prefill_chunk_append -- the chunk's cache write and its
+ * attention in one launch.  The pages store a chunk's new K/V with the fused
+ * reshape-and-write kernel before attending to them (review section 5.1,
+ * item 1; notes section 4.1).  This call instead reads the chunk's keys from
+ * key/value and writes them into the cache from the same kernel.
+ *
+ * Token t = cu_q_lens[s] + j of sequence s (position c + j, c as above) has
+ * its K and V rows at key + t*key_token_stride and value +
+ * t*value_token_stride ([num_heads][head_dim] each; strides in elements,
+ * >= num_heads*head_dim and whole 16-byte units, so slices of a fused QKV
+ * tensor work).  The call leaves the caches and `out` byte for byte as
+ *     pa_reshape_and_cache(key, value, ..., slot_mapping) with
+ *         slot_mapping[t] = block_tables[s][(c+j)/B] * B + (c+j) % B,
+ *     then pa_paged_attention_prefill_chunk(...)
+ * would.  Tokens whose table entry lies outside [0, num_blocks) are not
+ * written (the two calls skip them too).
+ *
+ * fp16 and bf16 at head_dim 128 only (the matrix-core kernel);
+ * PA_ERR_UNSUPPORTED otherwise.  Beyond pa_paged_attention_prefill_chunk's
+ * preconditions: the blocks the chunk writes are not read by another
+ * sequence of the batch, and key/value do not overlap the caches.  Under
+ * PA_DEBUG_VALIDATE the checks of pa_paged_attention_prefill_chunk apply.
+ */
+pa_status pa_paged_attention_prefill_chunk_append(void *out, const void *q, const void *key,
+                                                  const void *value, int64_t key_token_stride,
+                                                  int64_t value_token_stride,
+                                                  const int32_t *cu_q_lens, void *k_cache,
+                                                  void *v_cache, const int32_t *block_tables,
+                                                  int32_t max_blocks_per_seq,
+                                                  const int32_t *context_lens, int32_t num_seqs,
+                                                  int32_t total_q, int32_t max_q_len,
+                                                  int32_t max_context_len, int32_t num_heads,
+                                                  int32_t head_dim, int32_t block_size,
+                                                  int64_t num_blocks, float scale, pa_dtype dtype,
+                                                  void *stream);
+
+/*
  * pa_swap_blocks -- batched whole-block copy between two pools, for swapping
  * blocks out to host memory and back in (paper notes "PagedAttention:
  * Efficient Memory Management for Large Language Model Serving", sections

@@ -30,6 +30,7 @@ from ._binding import (  # noqa: F401
     paged_attention_decode_reduce,
     paged_attention_decode_shared,
     paged_attention_prefill_chunk,
+    paged_attention_prefill_chunk_append,
     reshape_and_cache,
     stream_read,
     swap_blocks,

@@ -48,6 +48,9 @@ _SIGS = {
     "pa_copy_blocks": ([P, P, i32, P, i64, i64, i64, P], ctypes.c_int),
     "pa_paged_attention_prefill_chunk": (
         [P, P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, P], ctypes.c_int),
+    "pa_paged_attention_prefill_chunk_append": (
+        [P, P, P, P, i64, i64, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, P],
+        ctypes.c_int),
     "pa_stream_read": ([P, i64, P, i32, P], ctypes.c_int),
     "pa_swap_blocks": ([P, P, i32, P, i64, i64, i64, i64, P], ctypes.c_int),
     "pa_decode_shared_workspace_bytes": ([i32, i32, i32, i32, i32, i32, i32, i32], sz),
@@ -351,13 +354,7 @@ def swap_blocks(src_caches: Sequence[torch.Tensor], dst_caches: Sequence[torch.T
                                int(dst_caches[0].shape[0]), _stream(stream)), "swap_blocks")
 
 
-def paged_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, cu_q_lens: torch.Tensor,
-                                  k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
-                                  context_lens: torch.Tensor, max_q_len: int, max_context_len: int, scale: float,
-                                  stream=None) -> torch.Tensor:
-    """Causal attention of each sequence's chunk of queries (rows
-    cu_q_lens[s]..cu_q_lens[s+1]) over its paged cache; context_lens include
-    the chunk, whose K/V must already be cached."""
+def _prefill_dims(out, q, cu_q_lens, k_cache, v_cache, block_tables, context_lens):
     N, H, B, D = _cache_dims(k_cache, v_cache)
     T = int(q.shape[0])
     S = int(context_lens.shape[0])
@@ -368,11 +365,47 @@ def paged_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, cu_q_lens:
         _contig(t, n)
     if cu_q_lens.shape != (S + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != S:
         raise ValueError("cu_q_lens must be [num_seqs+1] and block_tables [num_seqs, max_blocks]")
+    return N, H, B, D, T, S
+
+
+def paged_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, cu_q_lens: torch.Tensor,
+                                  k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                  context_lens: torch.Tensor, max_q_len: int, max_context_len: int, scale: float,
+                                  stream=None) -> torch.Tensor:
+    """Causal attention of each sequence's chunk of queries (rows
+    cu_q_lens[s]..cu_q_lens[s+1]) over its paged cache; context_lens include
+    the chunk, whose K/V must already be cached."""
+    N, H, B, D, T, S = _prefill_dims(out, q, cu_q_lens, k_cache, v_cache, block_tables, context_lens)
     _check(_lib.pa_paged_attention_prefill_chunk(
         _dev(out, "out"), _dev(q, "q"), _dev(cu_q_lens, "cu_q_lens", torch.int32), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
         _dev(context_lens, "context_lens", torch.int32), S, T, int(max_q_len), int(max_context_len), H, D, B, N,
         float(scale), _pa_dtype(q), _stream(stream)), "paged_attention_prefill_chunk")
+    return out
+
+
+def paged_attention_prefill_chunk_append(out: torch.Tensor, q: torch.Tensor, key: torch.Tensor,
+                                         value: torch.Tensor, cu_q_lens: torch.Tensor, k_cache: torch.Tensor,
+                                         v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                         context_lens: torch.Tensor, max_q_len: int, max_context_len: int,
+                                         scale: float, stream=None) -> torch.Tensor:
+    """The chunk's cache write and its attention in one launch: key / value
+    ([total_q, H, D], token-strided views allowed) are the chunk tokens' K/V,
+    written into their cache slots and attended over. Same caches and output
+    bytes as reshape_and_cache at those slots followed by
+    paged_attention_prefill_chunk (fp16/bf16, head_dim 128)."""
+    N, H, B, D, T, S = _prefill_dims(out, q, cu_q_lens, k_cache, v_cache, block_tables, context_lens)
+    for name, t in (("key", key), ("value", value)):
+        if t.shape != (T, H, D) or t.dtype != k_cache.dtype:
+            raise ValueError(f"{name} must be [{T}, {H}, {D}] {k_cache.dtype}")
+        if T and (t.stride(2) != 1 or t.stride(1) != D):
+            raise ValueError(f"{name}: heads and head_dim must be contiguous within a token")
+    _check(_lib.pa_paged_attention_prefill_chunk_append(
+        _dev(out, "out"), _dev(q, "q"), _dev(key, "key"), _dev(value, "value"), key.stride(0), value.stride(0),
+        _dev(cu_q_lens, "cu_q_lens", torch.int32), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(context_lens, "context_lens", torch.int32), S, T, int(max_q_len), int(max_context_len), H, D, B, N,
+        float(scale), _pa_dtype(q), _stream(stream)), "paged_attention_prefill_chunk_append")
     return out
 
 

@@ -290,7 +290,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t he
 // The newest token's rows for the fused append (decode_impl's `app`).
 struct AppendRows {
   const void *key, *value;
-  int64_t key_stride, value_stride;  // elements between sequences' rows
+  int64_t key_stride, value_stride;  // elements between rows (sequences for decode, tokens for prefill)
 };
 
 static pa_status decode_impl(bool run_parts, bool run_reduce, void *out, const void *q, const void *k_cache,
@@ -530,13 +530,12 @@ pa_status pa_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t n
                     "copy_blocks");
 }
 
-pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32_t *cu_q_lens, const void *k_cache,
-                                           const void *v_cache, const int32_t *block_tables,
-                                           int32_t max_blocks_per_seq, const int32_t *context_lens,
-                                           int32_t num_seqs, int32_t total_q, int32_t max_q_len,
-                                           int32_t max_context_len, int32_t num_heads, int32_t head_dim,
-                                           int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
-                                           void *stream) {
+static pa_status prefill_impl(void *out, const void *q, const int32_t *cu_q_lens, const void *k_cache,
+                              const void *v_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                              const int32_t *context_lens, int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                              int32_t max_context_len, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                              int64_t num_blocks, float scale, pa_dtype dtype, void *stream,
+                              const AppendRows *app = nullptr) {
   if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARG, "dtype %d is not one of PA_F32/PA_F16/PA_BF16", dtype);
   if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_context_len < 0 || num_heads <= 0 || head_dim <= 0 ||
       block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
@@ -544,14 +543,27 @@ pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32
   if (!pa::prefill_supported(dtype, head_dim, block_size))
     return fail(PA_ERR_UNSUPPORTED, "prefill chunk is built for head_dim 64/128 and block_size 4/8/16/32/64 "
                 "(got dtype %d, head_dim %d, block_size %d)", dtype, head_dim, block_size);
+  if (app && !pa::prefill_append_supported(dtype, head_dim, block_size))
+    return fail(PA_ERR_UNSUPPORTED, "the fused chunk write runs on the matrix-core kernel: fp16/bf16, head_dim 128 "
+                "(got dtype %d, head_dim %d)", dtype, head_dim);
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
   if (num_seqs > 65535 || num_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "grid dimension exceeds 65535");
+  if (app) {
+    const int64_t row = (int64_t)num_heads * head_dim;
+    if (app->key_stride < row || app->value_stride < row)
+      return fail(PA_ERR_INVALID_ARG, "token strides (%lld, %lld) smaller than num_heads*head_dim %lld",
+                  (long long)app->key_stride, (long long)app->value_stride, (long long)row);
+    if ((app->key_stride * elt_bytes(dtype)) % 16 != 0 || (app->value_stride * elt_bytes(dtype)) % 16 != 0)
+      return fail(PA_ERR_INVALID_ARG, "token strides must be whole 16-byte units");
+  }
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return ok();
-  if (!out || !q || !cu_q_lens || !k_cache || !v_cache || !block_tables || !context_lens)
+  if (!out || !q || !cu_q_lens || !k_cache || !v_cache || !block_tables || !context_lens ||
+      (app && (!app->key || !app->value)))
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-    return fail(PA_ERR_INVALID_ARG, "out, q and caches must be 16-byte aligned");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (app && (!aligned16(app->key) || !aligned16(app->value))))
+    return fail(PA_ERR_INVALID_ARG, "out, q, caches (and key, value) must be 16-byte aligned");
   pa::PrefillArgs a;
   a.out = out;
   a.q = q;
@@ -570,6 +582,10 @@ pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32
   if ((int64_t)max_blocks_per_seq * block_size < cap) cap = (int64_t)max_blocks_per_seq * block_size;
   a.ctx_cap = (int32_t)cap;
   a.scale_log2 = scale * kLog2e;
+  a.new_key = app ? app->key : nullptr;
+  a.new_value = app ? app->value : nullptr;
+  a.new_key_stride = app ? app->key_stride * elt_bytes(dtype) : 0;
+  a.new_value_stride = app ? app->value_stride * elt_bytes(dtype) : 0;
   if (pa::debug_validate()) {
     const pa_status vs = pa::validate_prefill(cu_q_lens, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                                               total_q, max_q_len, max_context_len, block_size, num_blocks,
@@ -578,6 +594,32 @@ pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32
   }
   return hip_status(pa::launch_prefill_chunk(a, dtype, head_dim, block_size, reinterpret_cast<hipStream_t>(stream)),
                     "prefill chunk");
+}
+
+pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32_t *cu_q_lens, const void *k_cache,
+                                           const void *v_cache, const int32_t *block_tables,
+                                           int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                           int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                           int32_t max_context_len, int32_t num_heads, int32_t head_dim,
+                                           int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
+                                           void *stream) {
+  return prefill_impl(out, q, cu_q_lens, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                      total_q, max_q_len, max_context_len, num_heads, head_dim, block_size, num_blocks, scale, dtype,
+                      stream);
+}
+
+pa_status pa_paged_attention_prefill_chunk_append(void *out, const void *q, const void *key, const void *value,
+                                                  int64_t key_token_stride, int64_t value_token_stride,
+                                                  const int32_t *cu_q_lens, void *k_cache, void *v_cache,
+                                                  const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                                  const int32_t *context_lens, int32_t num_seqs, int32_t total_q,
+                                                  int32_t max_q_len, int32_t max_context_len, int32_t num_heads,
+                                                  int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                                  float scale, pa_dtype dtype, void *stream) {
+  const AppendRows app{key, value, key_token_stride, value_token_stride};
+  return prefill_impl(out, q, cu_q_lens, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                      total_q, max_q_len, max_context_len, num_heads, head_dim, block_size, num_blocks, scale, dtype,
+                      stream, &app);
 }
 
 pa_status pa_swap_blocks(const void *const *src_caches, void *const *dst_caches, int32_t num_caches,

@@ -107,6 +107,15 @@ struct PrefillArgs {
   int32_t num_heads;
   int32_t ctx_cap;
   float scale_log2;
+  // Fused cache write only (both null otherwise): the chunk's K and V rows
+  // ([total_q][H][D], new_*_stride bytes apart).  The kernel reads the
+  // chunk's keys from them instead of the cache, and each workgroup writes
+  // the rows of its own queries' tokens into the cache (k_cache / v_cache
+  // are then writable).
+  const void *new_key;
+  const void *new_value;
+  int64_t new_key_stride;
+  int64_t new_value_stride;
 };
 
 // Shared-prefix decode (pa_shared.hip): members per group, prefix tiles per
@@ -144,6 +153,9 @@ hipError_t launch_shared_phases(const SharedArgs &a, int dtype, int head_dim, in
                                 bool combine, hipStream_t stream);
 
 bool prefill_supported(int dtype, int head_dim, int block_size);
+// Shapes whose prefill runs on the matrix-core kernel (the only one with the
+// fused chunk write).
+bool prefill_append_supported(int dtype, int head_dim, int block_size);
 // fp32 and head_dim 64 prefill (pa_prefill_general.hip).
 bool prefill_general_supported(int dtype, int head_dim, int block_size);
 hipError_t launch_prefill_general(const PrefillArgs &a, int dtype, int head_dim, int block_size, hipStream_t stream);

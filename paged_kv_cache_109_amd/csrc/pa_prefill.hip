@@ -120,7 +120,12 @@ __device__ __forceinline__ void load_lds16(const char *src, const lds_char *dst)
 
 }  // namespace
 
-template <Dt T, int B>
+// kAppend: the chunk's own K/V come from a.new_key / a.new_value.  Every
+// workgroup of a (sequence, head) reads the chunk's keys from those rows
+// (never from the cache), and after its main loop each workgroup copies the
+// rows of its own queries' tokens into their cache slots, so each token is
+// written once and no workgroup reads a cache row another one writes.
+template <Dt T, int B, bool kAppend>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu, kWavesPerEu))) void
 prefill_chunk_kernel(PrefillArgs a, int qtiles) {
   // The LDS ring: one array per slot, so the compiler can tell the slot a
@@ -237,6 +242,13 @@ prefill_chunk_kernel(PrefillArgs a, int qtiles) {
       e[i] = (v >= 0 && (int64_t)v < a.num_blocks) ? (uint32_t)v : 0u;
     }
   };
+  // Append: a chunk key (position >= c) is row q0 + key - c of the new rows;
+  // its offsets from the cache bases, valid while that row lies in q (the
+  // row index comes from device data).
+  [[maybe_unused]] const int64_t knew = kAppend ? (int64_t)((uintptr_t)a.new_key - (uintptr_t)kbase) +
+                                                      (int64_t)h * (kPfD * 2) + chunk_off : 0;
+  [[maybe_unused]] const int64_t vnew = kAppend ? (int64_t)((uintptr_t)a.new_value - (uintptr_t)vbase) +
+                                                      (int64_t)h * (kPfD * 2) + chunk_off : 0;
   auto load_block = [&](int kb, const uint32_t (&e)[kLoads], auto sc) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
@@ -244,8 +256,17 @@ prefill_chunk_kernel(PrefillArgs a, int qtiles) {
       const uint64_t blk = (uint64_t)e[i] * block_stride;
       const uint32_t off = (uint32_t)((key & (B - 1)) * kRow) + chunk_off;
       const int dst = 1024 * (wave + kPfWaves * i);
-      load_lds16(kbase + blk + off, (const lds_char *)(kslot(sc) + dst));
-      load_lds16(vbase + blk + off, (const lds_char *)(vslot(sc) + dst));
+      if constexpr (kAppend) {
+        const int row = q0 + key - c;
+        const bool fresh = key >= c && q0 >= 0 && row < a.total_q;
+        const int64_t ko = fresh ? knew + (int64_t)row * a.new_key_stride : (int64_t)(blk + off);
+        const int64_t vo = fresh ? vnew + (int64_t)row * a.new_value_stride : (int64_t)(blk + off);
+        load_lds16(kbase + ko, (const lds_char *)(kslot(sc) + dst));
+        load_lds16(vbase + vo, (const lds_char *)(vslot(sc) + dst));
+      } else {
+        load_lds16(kbase + blk + off, (const lds_char *)(kslot(sc) + dst));
+        load_lds16(vbase + blk + off, (const lds_char *)(vslot(sc) + dst));
+      }
     }
   };
 
@@ -450,6 +471,37 @@ prefill_chunk_kernel(PrefillArgs a, int qtiles) {
       *reinterpret_cast<uint2 *>(orow + (16 * dt + 4 * g) * 2) = w;
     }
   }
+
+  // ---- append: write the K/V rows of this tile's tokens (chunk indices
+  // qbase .. qbase+kPfQ-1) into their cache slots.  Thread t moves 16-byte
+  // chunk t % 32 (K for 0..15, V for 16..31) of kCopyRows rows; every load
+  // is issued before the first store.  Rows outside the context or q, and
+  // tokens whose table entry lies outside the pool, are skipped.
+  if constexpr (kAppend) {
+    constexpr int kCopyRows = kPfQ * 32 / kPfThreads;
+    const int part = tid % 32, is_v = part / 16, ch = part % 16;
+    uint4 rowv[kCopyRows];
+    int64_t dsto[kCopyRows];
+#pragma unroll
+    for (int u = 0; u < kCopyRows; ++u) {
+      const int j = qbase + tid / 32 + (kPfThreads / 32) * u;  // chunk index of the token
+      const int p = c + j;
+      const int row = q0 + j;
+      const bool live = j < q_len && p >= 0 && p < n && q0 >= 0 && row < a.total_q;
+      int32_t e = -1;
+      if (live) e = a.block_tables[table_row + p / B];
+      dsto[u] = (e >= 0 && (int64_t)e < a.num_blocks)
+                    ? (int64_t)e * block_stride + (int64_t)(p % B) * (kPfD * 2) + ch * 16
+                    : -1;
+      const char *src = reinterpret_cast<const char *>(is_v ? a.new_value : a.new_key) +
+                        (int64_t)(live ? row : 0) * (is_v ? a.new_value_stride : a.new_key_stride) +
+                        (int64_t)h * (kPfD * 2) + ch * 16;
+      rowv[u] = load16(src);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyRows; ++u)
+      if (dsto[u] >= 0) *reinterpret_cast<uint4 *>(const_cast<char *>(is_v ? vbase : kbase) + dsto[u]) = rowv[u];
+  }
 }
 
 static bool prefill_mfma_supported(int dtype, int head_dim, int block_size) {
@@ -465,7 +517,10 @@ static hipError_t launch_pf(const PrefillArgs &a, hipStream_t st) {
   const int64_t groups = (pairs + 7) / 8;
   const int64_t grid = groups * 8 * qtiles;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_chunk_kernel<T, B>), dim3((unsigned)grid), dim3(kPfThreads), 0, st, a, qtiles);
+  if (a.new_key)
+    hipLaunchKernelGGL((prefill_chunk_kernel<T, B, true>), dim3((unsigned)grid), dim3(kPfThreads), 0, st, a, qtiles);
+  else
+    hipLaunchKernelGGL((prefill_chunk_kernel<T, B, false>), dim3((unsigned)grid), dim3(kPfThreads), 0, st, a, qtiles);
   return hipGetLastError();
 }
 
@@ -481,6 +536,10 @@ static hipError_t launch_pf_b(const PrefillArgs &a, int B, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+bool prefill_append_supported(int dtype, int head_dim, int block_size) {
+  return prefill_mfma_supported(dtype, head_dim, block_size);
+}
+
 bool prefill_supported(int dtype, int head_dim, int block_size) {
   return prefill_mfma_supported(dtype, head_dim, block_size) || prefill_general_supported(dtype, head_dim, block_size);
 }
@@ -491,8 +550,8 @@ hipError_t launch_prefill_chunk(const PrefillArgs &a, int dtype, int head_dim, i
     if (dtype == (int)Dt::BF16) return launch_pf_b<Dt::BF16>(a, block_size, stream);
     return launch_pf_b<Dt::F16>(a, block_size, stream);
   }
-  // fp32, or head_dim 64: the vector-ALU kernel.
-  if (prefill_general_supported(dtype, head_dim, block_size))
+  // fp32, or head_dim 64: the vector-ALU kernel (which has no fused write).
+  if (!a.new_key && prefill_general_supported(dtype, head_dim, block_size))
     return launch_prefill_general(a, dtype, head_dim, block_size, stream);
   return hipErrorInvalidValue;
 }

@@ -171,3 +171,22 @@ def test_shared_decode_rejects_bad_arguments():
     n = B._lib.pa_decode_shared_workspace_bytes
     assert n(2, 4, 128, 100, 16, 1, 32, 7) > B._lib.pa_decode_workspace_bytes(2, 4, 128, 100, 16, 7)
     assert n(0, 4, 128, 100, 16, 1, 32, 7) == 0
+
+
+def prefill_append(**over):
+    a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, ks=5120, vs=5120, cu=FAKE, k=FAKE, v=FAKE, bt=FAKE, M=8,
+             ctx=FAKE, S=2, T=64, maxq=32, maxc=100, H=40, D=128, Bs=16, N=64, scale=0.1, dt=2, stream=None)
+    a.update(over)
+    return B._lib.pa_paged_attention_prefill_chunk_append(
+        a["out"], a["q"], a["key"], a["value"], a["ks"], a["vs"], a["cu"], a["k"], a["v"], a["bt"], a["M"],
+        a["ctx"], a["S"], a["T"], a["maxq"], a["maxc"], a["H"], a["D"], a["Bs"], a["N"], a["scale"], a["dt"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dt=0), 2), (dict(D=64, ks=2560, vs=2560), 2), (dict(Bs=12), 2), (dict(scale=-1.0), 1),
+    (dict(key=None), 1), (dict(value=FAKE + 8), 1), (dict(ks=5119), 1), (dict(vs=5124), 1), (dict(k=None), 1),
+])
+def test_prefill_append_rejects_bad_arguments(over, status):
+    assert prefill_append(**over) == status
+    assert B._lib.pa_last_error()
