@@ -496,12 +496,19 @@ def bench_prefill(args):
     calibrate_counters(torch, dev)
     stream_read = measure_stream_read(torch, pa, dev)
 
+    fused = args.step == "fused"
+
     def step(i, ev=None):
         k_cache, v_cache = pools[i % len(pools)]
-        pa.reshape_and_cache(nk, nv, k_cache, v_cache, slots)
+        if not fused:
+            pa.reshape_and_cache(nk, nv, k_cache, v_cache, slots)
         if ev is not None:
             ev[0].record(stream)
-        pa.paged_attention_prefill_chunk(out, q, cu, k_cache, v_cache, bt, ctx, max_q, max_ctx, case.scale)
+        if fused:
+            pa.paged_attention_prefill_chunk_append(out, q, nk, nv, cu, k_cache, v_cache, bt, ctx, max_q, max_ctx,
+                                                    case.scale)
+        else:
+            pa.paged_attention_prefill_chunk(out, q, cu, k_cache, v_cache, bt, ctx, max_q, max_ctx, case.scale)
         if ev is not None:
             ev[1].record(stream)
 
@@ -523,8 +530,10 @@ def bench_prefill(args):
     elt = 2
     kv_bytes = W.logical_kv_bytes(case.context_lens, H, D, elt)
     qo_bytes = 2 * int(q_lens.sum()) * H * D * elt
+    # Fused, the launch also writes the chunk's K and V rows into the cache.
+    write_bytes = 2 * int(q_lens.sum()) * H * D * elt if fused else 0
     tflops = flops / kern_s / 1e12
-    gbps = (kv_bytes + qo_bytes) / kern_s / 1e9
+    gbps = (kv_bytes + qo_bytes + write_bytes) / kern_s / 1e9
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -544,13 +553,15 @@ def bench_prefill(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": case.name, "num_seqs": S, "q_len": max_q, "num_heads": H, "head_dim": D,
                    "block_size": B, "context_tokens": int(case.context_lens.sum()),
-                   "step": "reshape_and_cache(4096 chunk tokens) + prefill chunk kernel",
+                   "step": ("prefill chunk kernel with the 4096 chunk tokens' cache write fused in" if fused
+                            else "reshape_and_cache(4096 chunk tokens) + prefill chunk kernel"),
                    "pool_replicas": len(pools), "step_launch": launch},
         "stream_read": stream_read,
-        "roofline": {"bound": "hbm", "kernel": "prefill_chunk_kernel", "achieved": gbps, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
-                     "traffic": committed_traffic("prefill_chunk_chunked_prefill", "pa_prefill.hip"),
-                     "alg_bytes_per_launch": kv_bytes + qo_bytes, "avg_launch_us": kern_s * 1e6,
+        "roofline": {"bound": "hbm", "kernel": "prefill_chunk_kernel" + (" (append)" if fused else ""),
+                     "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                     "traffic": committed_traffic("prefill_chunk_" + ("append_" if fused else "") + "chunked_prefill",
+                                                  "pa_prefill.hip"),
+                     "alg_bytes_per_launch": kv_bytes + qo_bytes + write_bytes, "avg_launch_us": kern_s * 1e6,
                      **launch_stats(kern_ms), "frac_of_stream_read": gbps / stream_read["gbps"],
                      "mfma_tflops": tflops, "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                      "mfma_frac": tflops / MFMA_BF16_PEAK_TFLOPS, "causal_flops_per_launch": flops},
