@@ -141,3 +141,40 @@ def test_decode_append_step_graph_replays_match_eager():
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
         assert torch.equal(dc.k_cache[blk, :, off].view(torch.int16), nk.view(torch.int16))
         assert torch.equal(dc.v_cache[blk, :, off].view(torch.int16), nv.view(torch.int16))
+
+
+def test_prefill_append_step_graph_replays_match_eager():
+    c = W.make_prefill_case(3, 0, [0, 500, 1300], 4, 128, 16, "bf16", seed=6, q_lens=[100, 256, 37])
+    dc = DeviceCase(c)
+    nk, nv = dev(c.new_key, c.dtype), dev(c.new_value, c.dtype)
+    cu = dev(c.cu_q_lens)
+    max_q = int(np.diff(c.cu_q_lens).max())
+    slots = oracle.slots(c.block_tables, c.new_seq, c.new_pos, c.block_size)
+    out = torch.empty_like(dc.q)
+
+    def step():
+        pa.paged_attention_prefill_chunk_append(out, dc.q, nk, nv, cu, dc.k_cache, dc.v_cache, dc.block_tables,
+                                                dc.context_lens, max_q, c.max_context_len, c.scale)
+
+    say("  prefill append step: eager")
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    oracle.reshape_and_cache(c.k_cache, c.v_cache, c.new_key, c.new_value, slots, c.dtype)
+    check_attention(eager, oracle.prefill_chunk(c.q, c.cu_q_lens, c.k_cache, c.v_cache, c.block_tables,
+                                                c.context_lens, c.scale, c.dtype), c.dtype, "eager prefill append")
+    blk = torch.from_numpy(slots // 16).cuda()
+    off = torch.from_numpy(slots % 16).cuda()
+    g = capture(step)
+    for r in range(4):
+        # Clobber the output and the rows the step writes (it never reads them).
+        out.fill_(float("nan"))
+        dc.k_cache[blk, :, off] = float("nan")
+        dc.v_cache[blk, :, off] = float("nan")
+        torch.cuda.synchronize()
+        say(f"  prefill append step: replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
+        assert torch.equal(dc.k_cache[blk, :, off].view(torch.int16), nk.view(torch.int16))
+        assert torch.equal(dc.v_cache[blk, :, off].view(torch.int16), nv.view(torch.int16))
