@@ -218,3 +218,31 @@ def test_decode_append(validate):
             "context_lens[3] = 64")
     torch.cuda.synchronize()
     assert bool((sentinel == 7.0).all()) and torch.equal(k4, k) and torch.equal(v4, v)
+
+
+def test_prefill_chunk_append(validate):
+    c = W.make_prefill_case(2, 0, [30, 5], 2, 128, 16, "bf16", seed=4, q_lens=[10, 7], name="validate_append")
+    q, k, v = dev(c.q, "bf16"), dev(c.k_cache, "bf16"), dev(c.v_cache, "bf16")
+    nk, nv = dev(c.new_key, "bf16"), dev(c.new_value, "bf16")
+    cu, bt, ctx = dev(c.cu_q_lens), dev(c.block_tables), dev(c.context_lens)
+    max_ctx = int(c.context_lens.max())
+
+    def call(out, kc, vc, bt=bt):
+        return pa.paged_attention_prefill_chunk_append(out, q, nk, nv, cu, kc, vc, bt, ctx, 10, max_ctx, c.scale)
+
+    k1, v1 = k.clone(), v.clone()
+    out = call(torch.empty_like(q), k1, v1)
+    torch.cuda.synchronize()
+    k2, v2, plain = k.clone(), v.clone(), torch.empty_like(q)
+    with pytest.MonkeyPatch.context() as m:
+        m.delenv("PA_DEBUG_VALIDATE")
+        call(plain, k2, v2)
+        torch.cuda.synchronize()
+    assert torch.equal(out, plain) and torch.equal(k1, k2) and torch.equal(v1, v2)
+
+    sentinel, k3, v3 = torch.full_like(q, 7.0), k.clone(), v.clone()
+    bad = bt.clone()
+    bad[0, 2] = c.k_cache.shape[0]
+    refused(lambda: call(sentinel, k3, v3, bt=bad), "block_tables[0][2]")
+    torch.cuda.synchronize()
+    assert bool((sentinel == 7.0).all()) and torch.equal(k3, k) and torch.equal(v3, v)
