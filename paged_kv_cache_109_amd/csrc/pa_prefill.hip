@@ -473,34 +473,61 @@ prefill_chunk_kernel(PrefillArgs a, int qtiles) {
   }
 
   // ---- append: write the K/V rows of this tile's tokens (chunk indices
-  // qbase .. qbase+kPfQ-1) into their cache slots.  Thread t moves 16-byte
-  // chunk t % 32 (K for 0..15, V for 16..31) of kCopyRows rows; every load
-  // is issued before the first store.  Rows outside the context or q, and
-  // tokens whose table entry lies outside the pool, are skipped.
+  // qbase .. qbase+kPfQ-1, keys tok_lo .. tok_hi-1) into their cache slots.
+  // The ring still holds the last four blocks, loaded from the new rows:
+  // each lane stores the 16 bytes it loaded there for every such key.  Keys
+  // in an older block (at most kPfKeys-1 of them, when the tile does not
+  // start on a block) are copied from the new rows.  Tokens outside the
+  // context or q, or whose table entry lies outside the pool, are skipped.
   if constexpr (kAppend) {
-    constexpr int kCopyRows = kPfQ * 32 / kPfThreads;
-    const int part = tid % 32, is_v = part / 16, ch = part % 16;
-    uint4 rowv[kCopyRows];
-    int64_t dsto[kCopyRows];
+    const int tok_lo = max(c + qbase, 0), tok_hi = min(c + qbase + kPfQ, n);
+    const int ring_lo = max(nkb - kPfRing, 0) * kPfKeys;  // first key still in the ring
+    auto store_slot = [&](auto sc) __attribute__((always_inline)) {
+      constexpr int j = decltype(sc)::value;
+      // The block in slot j: the last one below nkb that is j mod 4.
+      const int b = nkb - 1 - (((nkb - 1 - j) % kPfRing) + kPfRing) % kPfRing;
+      const int key = b * kPfKeys + r0;
+      const int key0 = b * kPfKeys + 4 * wave;  // the wave's 4 rows share one table entry
+      if (b >= 0 && key >= tok_lo && key < tok_hi && key < kv_end && q0 >= 0 && q0 + key - c < a.total_q) {
+        const int32_t e = a.block_tables[table_row + key0 / B];
+        if (e >= 0 && (int64_t)e < a.num_blocks) {
+          const int64_t d = (int64_t)e * block_stride + (int64_t)(key & (B - 1)) * kRow + chunk_off;
+          const int l = 1024 * wave + 16 * lane;
+          *reinterpret_cast<uint4 *>(const_cast<char *>(kbase) + d) = *reinterpret_cast<const uint4 *>(kslot(sc) + l);
+          *reinterpret_cast<uint4 *>(const_cast<char *>(vbase) + d) = *reinterpret_cast<const uint4 *>(vslot(sc) + l);
+        }
+      }
+    };
+    store_slot(S0{});
+    store_slot(S1{});
+    store_slot(S2{});
+    store_slot(S3{});
+    if (tok_lo < min(tok_hi, ring_lo)) {  // workgroup-uniform
+      constexpr int kCopyRows = kPfQ * 32 / kPfThreads;
+      const int part = tid % 32, is_v = part / 16, ch = part % 16;
+      uint4 rowv[kCopyRows];
+      int64_t dsto[kCopyRows];
 #pragma unroll
-    for (int u = 0; u < kCopyRows; ++u) {
-      const int j = qbase + tid / 32 + (kPfThreads / 32) * u;  // chunk index of the token
-      const int p = c + j;
-      const int row = q0 + j;
-      const bool live = j < q_len && p >= 0 && p < n && q0 >= 0 && row < a.total_q;
-      int32_t e = -1;
-      if (live) e = a.block_tables[table_row + p / B];
-      dsto[u] = (e >= 0 && (int64_t)e < a.num_blocks)
-                    ? (int64_t)e * block_stride + (int64_t)(p % B) * (kPfD * 2) + ch * 16
-                    : -1;
-      const char *src = reinterpret_cast<const char *>(is_v ? a.new_value : a.new_key) +
-                        (int64_t)(live ? row : 0) * (is_v ? a.new_value_stride : a.new_key_stride) +
-                        (int64_t)h * (kPfD * 2) + ch * 16;
-      rowv[u] = load16(src);
+      for (int u = 0; u < kCopyRows; ++u) {
+        const int j = qbase + tid / 32 + (kPfThreads / 32) * u;  // chunk index of the token
+        const int p = c + j;
+        const int row = q0 + j;
+        const bool live = j < q_len && p >= 0 && p < n && p < ring_lo && q0 >= 0 && row < a.total_q;
+        int32_t e = -1;
+        if (live) e = a.block_tables[table_row + p / B];
+        dsto[u] = (e >= 0 && (int64_t)e < a.num_blocks)
+                      ? (int64_t)e * block_stride + (int64_t)(p % B) * (kPfD * 2) + ch * 16
+                      : -1;
+        rowv[u] = make_uint4(0, 0, 0, 0);
+        if (dsto[u] >= 0)
+          rowv[u] = load16(reinterpret_cast<const char *>(is_v ? a.new_value : a.new_key) +
+                           (int64_t)row * (is_v ? a.new_value_stride : a.new_key_stride) + (int64_t)h * (kPfD * 2) +
+                           ch * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < kCopyRows; ++u)
+        if (dsto[u] >= 0) *reinterpret_cast<uint4 *>(const_cast<char *>(is_v ? vbase : kbase) + dsto[u]) = rowv[u];
     }
-#pragma unroll
-    for (int u = 0; u < kCopyRows; ++u)
-      if (dsto[u] >= 0) *reinterpret_cast<uint4 *>(const_cast<char *>(is_v ? vbase : kbase) + dsto[u]) = rowv[u];
   }
 }
 
