@@ -13,6 +13,9 @@ The timed steps are eager launches of the step's kernels with nothing else
 between the two events that bracket them. --graph replays the step captured
 once as a HIP graph instead (one graph per pool replica: the same kernels on
 the same buffers); on ROCm 7 that measured slower than eager launches.
+--step fused folds the cache write into the attention kernel (the decode
+pass with one new token per sequence, or the chunked prefill kernel) instead
+of launching reshape_and_cache first; the default keeps the two launches.
 
 Prints ONE JSON line. `value` is decode tokens/s for one layer call (one
 query token per sequence per step). `roofline` is for the dominant kernel,
