@@ -22,7 +22,9 @@
  *    the host-only block manager).  The library keeps no pointer after a
  *    call returns, allocates no device memory, and holds no mutable global
  *    state: calls are re-entrant (a block manager is an object of its own,
- *    created and destroyed by the caller).
+ *    created and destroyed by the caller).  The one exception is
+ *    pa_paged_attention_decode_noalloc, whose workspace is a fixed array
+ *    the library holds on each device.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on that stream and returns without synchronising.
  *  - Layouts are C-contiguous:
@@ -174,6 +176,34 @@ pa_status pa_paged_attention_decode(void *out, const void *q, const void *k_cach
                                     int32_t head_dim, int32_t block_size, int64_t num_blocks,
                                     float scale, pa_dtype dtype, int32_t split_workers,
                                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pa_paged_attention_decode_noalloc -- pa_paged_attention_decode without a
+ * caller workspace, for callers that cannot allocate device memory (code
+ * under stream capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, same kernels and the same output bytes as
+ * pa_paged_attention_decode with the same split_workers; the plan and the
+ * partial results live instead in a fixed array of PA_NOALLOC_SCRATCH_BYTES
+ * bytes that the library holds on every device it runs on until the process
+ * ends.  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine); its first call on a device looks the array's address up.
+ *
+ * The array needs no initialisation and keeps the last call's contents.
+ * Every call on one device shares it: calls that may overlap on a device
+ * (two streams, two threads) race and give wrong results -- order them on
+ * one stream.  A decode whose workspace (pa_decode_workspace_bytes with the
+ * same arguments) exceeds PA_NOALLOC_SCRATCH_BYTES is refused with
+ * PA_ERR_WORKSPACE before anything is enqueued; head_dim <= 128 at up to 32
+ * worker waves per compute unit on 256 compute units fits.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (16u << 20)
+pa_status pa_paged_attention_decode_noalloc(void *out, const void *q, const void *k_cache,
+                                            const void *v_cache, const int32_t *block_tables,
+                                            int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                            int32_t max_context_len, int32_t num_seqs,
+                                            int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                            int64_t num_blocks, float scale, pa_dtype dtype,
+                                            int32_t split_workers, void *stream);
 
 /*
  * pa_paged_attention_decode_append -- the decode step's cache write and its

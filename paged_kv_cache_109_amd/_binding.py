@@ -35,6 +35,8 @@ _SIGS = {
     "pa_decode_workspace_bytes": ([i32, i32, i32, i32, i32, i32], sz),
     "pa_paged_attention_decode": (
         [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, i32, P, sz, P], ctypes.c_int),
+    "pa_paged_attention_decode_noalloc": (
+        [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, i32, P], ctypes.c_int),
     "pa_paged_attention_decode_partitions": (
         [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, i32, P, sz, P], ctypes.c_int),
     "pa_paged_attention_decode_append": (
@@ -194,6 +196,22 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
     _check(_lib.pa_paged_attention_decode(*_decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
                                                         max_context_len, scale, split_workers, workspace,
                                                         stream)), "paged_attention_decode")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # PA_NOALLOC_SCRATCH_BYTES
+
+
+def paged_attention_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                                   v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                   max_context_len: int, scale: float, split_workers: int = 0,
+                                   stream=None) -> torch.Tensor:
+    """paged_attention_decode with the library's fixed per-device workspace
+    instead of a caller one: allocates nothing. Calls on one device share
+    that workspace, so they must not overlap (order them on one stream)."""
+    args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                        split_workers, None, stream)
+    _check(_lib.pa_paged_attention_decode_noalloc(*args[:16], args[-1]), "paged_attention_decode_noalloc")
     return out
 
 

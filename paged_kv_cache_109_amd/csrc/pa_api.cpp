@@ -358,6 +358,33 @@ pa_status pa_paged_attention_decode(void *out, const void *q, const void *k_cach
                      split_workers, workspace, workspace_bytes, stream);
 }
 
+pa_status pa_paged_attention_decode_noalloc(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                            const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                            const int32_t *context_lens, int32_t max_context_len,
+                                            int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                            int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype,
+                                            int32_t split_workers, void *stream) {
+  pa_status st = check_decode_common(k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                                     max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks,
+                                     dtype, split_workers);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return ok();
+  const DecodeGeometry g = geometry(head_dim, max_context_len, max_blocks_per_seq, block_size,
+                                    decode_workers(dtype, head_dim, block_size, split_workers));
+  if (g.ws_bytes > PA_NOALLOC_SCRATCH_BYTES)
+    return fail(PA_ERR_WORKSPACE,
+                "decode_noalloc: the call needs %zu bytes of workspace (%lld worker waves, head_dim %d), more than "
+                "the fixed %u-byte device array; pass a smaller split_workers or use pa_paged_attention_decode",
+                g.ws_bytes, (long long)g.workers, head_dim, (unsigned)PA_NOALLOC_SCRATCH_BYTES);
+  void *scratch = nullptr;
+  const hipError_t e = pa::noalloc_scratch(&scratch);
+  if (e != hipSuccess)
+    return fail(PA_ERR_HIP, "decode_noalloc: device address of the fixed workspace: %s", hipGetErrorString(e));
+  return decode_impl(true, true, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks, scale, dtype,
+                     split_workers, scratch, PA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 pa_status pa_paged_attention_decode_append(void *out, const void *q, const void *key, const void *value,
                                            int64_t key_seq_stride, int64_t value_seq_stride, void *k_cache,
                                            void *v_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,

@@ -38,6 +38,8 @@
 // each lane group keeps its own online-softmax state and fp32 value
 // accumulator, merged with lane swaps when a pair ends.
 
+#include <mutex>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -779,6 +781,37 @@ hipError_t launch_decode_reduce(const DecodeArgs &a, int dtype, int head_dim, hi
     case Dt::BF16: return launch_red<Dt::BF16>(a, head_dim, stream);
   }
   return hipErrorInvalidValue;
+}
+
+// ------------------------------------------- workspace of the no-alloc call
+
+// The plan and partial results of pa_paged_attention_decode_noalloc, for
+// callers that cannot allocate.  Each device holds its own copy of this
+// array from the library's load until the process ends.  In host code the
+// name is only a stand-in for it, never a device address: the address is
+// asked of the runtime once per device, with that device current, and only
+// that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t noalloc_scratch(void **ptr) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace pa

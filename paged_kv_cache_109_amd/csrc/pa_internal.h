@@ -68,6 +68,11 @@ hipError_t launch_decode_partitions(const DecodeArgs &a, int dtype, int head_dim
                                     hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream);
 
+// The allocation-free decode's workspace: a fixed device array of
+// PA_NOALLOC_SCRATCH_BYTES per device (pa_decode.hip).  Sets *ptr to the
+// current device's copy, looked up once per device.
+hipError_t noalloc_scratch(void **ptr);
+
 hipError_t launch_reshape_and_cache(const void *key, const void *value, int64_t key_stride_bytes,
                                     int64_t value_stride_bytes, void *k_cache, void *v_cache,
                                     const int64_t *slot_mapping, int64_t num_tokens, int32_t num_heads,

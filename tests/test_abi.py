@@ -68,6 +68,19 @@ def test_decode_rejects_bad_arguments(over, status):
     assert B._lib.pa_last_error()
 
 
+@pytest.mark.parametrize("over,status", [
+    (dict(dt=7), 1), (dict(H=0), 1), (dict(D=96), 2), (dict(k=None), 1), (dict(part=-1), 1), (dict(S=70000), 2),
+])
+def test_decode_noalloc_rejects_bad_arguments(over, status):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, M=8, ctx=FAKE, max_ctx=100, S=2, H=4, D=128, Bs=16, N=64,
+             scale=0.1, dt=1, part=0, stream=None)
+    a.update(over)
+    assert B._lib.pa_paged_attention_decode_noalloc(a["out"], a["q"], a["k"], a["v"], a["bt"], a["M"], a["ctx"],
+                                                    a["max_ctx"], a["S"], a["H"], a["D"], a["Bs"], a["N"],
+                                                    a["scale"], a["dt"], a["part"], a["stream"]) == status
+    assert B._lib.pa_last_error()
+
+
 def decode_append(partitions=False, **over):
     a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, ks=512, vs=512, k=FAKE, v=FAKE, bt=FAKE, M=8, ctx=FAKE,
              max_ctx=100, S=2, H=4, D=128, Bs=16, N=64, scale=0.1, dt=1, part=0, ws=None, ws_bytes=0, stream=None)
