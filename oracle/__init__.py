@@ -122,6 +122,39 @@ def slots(block_tables: np.ndarray, seq: np.ndarray, pos: np.ndarray, block_size
     return out
 
 
+def shared_prefix(block_tables: np.ndarray, context_lens, members: Sequence[int], block_size: int,
+                  tile: int = 16, lib=None) -> int:
+    """Tokens at the start of a group's contexts that live in the same
+    physical storage for every member.
+
+    Samples forked from one prompt point their tables at the prompt's
+    physical blocks (paper notes "PagedAttention: Efficient Memory Management
+    for Large Language Model Serving", section 3.4.1 Parallel sampling; "KV
+    캐시 관리와 PagedAttention", section on sharing the common KV of several
+    responses). Walked position by position: position p is held in common
+    when it is inside every member's context and the oracle's own address
+    translation of p gives one and the same slot for every member. The run
+    of common positions from 0 is then cut to whole blocks (a block read
+    for the group must be common in all of its positions) and to whole
+    tiles of `tile` tokens (the unit the decode reads), i.e. to a multiple
+    of lcm(block_size, tile)."""
+    import math
+    bt = _c(block_tables, np.int32)
+    ctx = _c(context_lens, np.int64)
+    members = [int(m) for m in members]
+    lib = lib or load()
+    bound = min(max(int(ctx[m]), 0) for m in members)
+    bound = min(bound, bt.shape[1] * block_size)
+    run = 0
+    while run < bound:
+        where = {int(lib.oracle_slot(bt[m].ctypes.data, run, int(block_size))) for m in members}
+        if len(where) != 1:
+            break
+        run += 1
+    unit = block_size * tile // math.gcd(block_size, tile)
+    return run // unit * unit
+
+
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, dtype: str,
            threads: int = 0, lib=None) -> np.ndarray:
     """Paged decode attention; returns float64 [num_seqs, num_heads, head_dim]."""
