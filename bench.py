@@ -244,7 +244,8 @@ def main():
     context_lens = to_dev(case.context_lens)
     writes = case.new_key is not None
     if writes:
-        slots = to_dev(pa.slot_mapping(case.block_tables, case.new_seq, case.new_pos, B))
+        slots = pa.slot_mapping(block_tables, to_dev(case.new_seq.astype(np.int32)),
+                                to_dev(case.new_pos.astype(np.int32)), B, case.num_blocks)
         new_k, new_v = to_dev(case.new_key, case.dtype), to_dev(case.new_value, case.dtype)
     copies = case.block_mapping is not None
     if copies:
@@ -490,7 +491,8 @@ def bench_prefill(args):
     # least four copies so each launch reads its K/V from HBM.
     pools = [(to_dev(case.k_cache, True), to_dev(case.v_cache, True)) for _ in range(max(4, args.replicas))]
     bt, ctx, cu = to_dev(case.block_tables), to_dev(case.context_lens), to_dev(case.cu_q_lens)
-    slots = to_dev(pa.slot_mapping(case.block_tables, case.new_seq, case.new_pos, B))
+    slots = pa.slot_mapping(bt, to_dev(case.new_seq.astype(np.int32)), to_dev(case.new_pos.astype(np.int32)), B,
+                            case.num_blocks)
     nk, nv = to_dev(case.new_key, True), to_dev(case.new_value, True)
     out = torch.empty_like(q)
     q_lens = np.diff(case.cu_q_lens)

@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -95,6 +95,36 @@ const char *pa_status_string(pa_status status);
 
 /* Detail of the last failed call on this thread ("" if none). */
 const char *pa_last_error(void);
+
+/*
+ * pa_slot_mapping -- the cache slot of each token a step writes.
+ *
+ * The address translation of "KV 캐시 관리와 PagedAttention"
+ * (llm-systems-engineering.pages.dev, section on linking token order to
+ * storage): position p of a sequence lies at offset p % B of its logical
+ * block p / B, the sequence's block table maps that logical block to a
+ * physical one, and the flat slot is physical * B + p % B -- the slot
+ * numbering pa_reshape_and_cache takes.  For every token t:
+ *     s = seq_ids[t], p = positions[t]
+ *     slot_mapping[t] = block_tables[s][p / B] * B + p % B
+ * or -1 (a token pa_reshape_and_cache skips) when s is outside
+ * [0, num_seqs), p < 0, p / B >= max_blocks_per_seq, or the table entry is
+ * outside [0, num_blocks).
+ *
+ *  block_tables   device int32 [num_seqs][max_blocks_per_seq].
+ *  seq_ids        device int32 [num_tokens]: the token's sequence.
+ *  positions      device int32 [num_tokens]: its position, from 0 (e.g. the
+ *                 newest token of a decode step is at context_len - 1).
+ *  slot_mapping   device int64 [num_tokens], written.
+ *  num_tokens     >= 0 (0 is a no-op).
+ * Errors: PA_ERR_INVALID_ARG for a null pointer with num_tokens > 0 or a
+ * non-positive size.  Runs on the device, so it may be enqueued under
+ * stream capture between the steps that produce the tables and the cache
+ * write that consumes the slots.
+ */
+pa_status pa_slot_mapping(const int32_t *block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                          const int32_t *seq_ids, const int32_t *positions, int64_t num_tokens,
+                          int32_t block_size, int64_t num_blocks, int64_t *slot_mapping, void *stream);
 
 /*
  * pa_reshape_and_cache -- write new K/V rows into their cache slots.
@@ -236,7 +266,9 @@ pa_status pa_paged_attention_decode_noalloc(void *out, const void *q, const void
  * position n - 1 of a sequence is not read by another sequence of the batch
  * (true of any copy-on-write table: a block written to has one owner), and
  * key/value do not overlap the caches.  Under PA_DEBUG_VALIDATE the table
- * and length checks of pa_paged_attention_decode apply.
+ * and length checks of pa_paged_attention_decode apply, and the written
+ * slots must be distinct and lie in blocks no other sequence of the batch
+ * reads (a shared block the caller forgot to copy is refused).
  */
 pa_status pa_paged_attention_decode_append(void *out, const void *q, const void *key,
                                            const void *value, int64_t key_seq_stride,
@@ -301,7 +333,8 @@ pa_status pa_paged_attention_decode_reduce(void *out, const int32_t *context_len
  *  group_prefix   device int32 [num_groups]: P, the tokens whose blocks all
  *                 members share (same physical block ids at the same table
  *                 entries), a multiple of 16 and of block_size, at most
- *                 every member's context length.
+ *                 every member's context length.  pa_shared_prefix_groups
+ *                 derives these three arrays from the tables.
  *  seq_starts     device int32 [num_seqs]: P of the sequence's group, 0 for
  *                 a sequence in no group (decoded as usual).
  *  max_prefix_len host upper bound of group_prefix.
@@ -323,6 +356,51 @@ pa_status pa_paged_attention_decode_reduce(void *out, const int32_t *context_len
  * the given arrays.
  */
 #define PA_MAX_GROUP_MEMBERS 8
+
+/*
+ * pa_shared_prefix_groups -- the sharing description that
+ * pa_paged_attention_decode_shared takes, derived from the block tables.
+ * Host only: all arrays are host memory, no GPU call.
+ *
+ * The caller names which sequences were forked from one prompt (paper notes,
+ * section 3.4.1 Parallel sampling: the samples point at the prompt's
+ * physical blocks).  For each such group the call finds P, the tokens of
+ * the leading table entries that every member holds identically (the same
+ * physical block at the same logical index) and has filled (every position
+ * of the block is below every member's context length), rounded down to a
+ * multiple of 16 (the decode's tile).  A group of more than
+ * PA_MAX_GROUP_MEMBERS sequences is split, in order, into groups of at most
+ * that many with the same P.
+ *
+ *  block_tables   [num_seqs][max_blocks_per_seq] int32; context_lens
+ *                 [num_seqs] int32 (negative lengths count as 0).
+ *  group_offsets  [num_groups + 1] int32, non-decreasing from 0: group g's
+ *                 members are group_seqs[group_offsets[g] ..
+ *                 group_offsets[g + 1]); an empty group is skipped.
+ *  group_seqs     int32 sequence ids in [0, num_seqs), each in at most one
+ *                 group.
+ *  max_out_groups capacity of the outputs below; num_groups +
+ *                 group_offsets[num_groups] / PA_MAX_GROUP_MEMBERS always
+ *                 suffices.
+ *  group_members  written: [*num_out_groups][PA_MAX_GROUP_MEMBERS], each row
+ *                 a leading run of sequence ids padded with -1.
+ *  group_prefix   written: [*num_out_groups], P of each output group.
+ *  seq_starts     written: [num_seqs], P of the sequence's group, 0 for a
+ *                 sequence in no group.
+ *  num_out_groups, max_prefix_len  written: the output group count and the
+ *                 largest P (0 without groups).
+ * Errors (nothing written): PA_ERR_INVALID_ARG for a null pointer, bad
+ * offsets, a sequence id out of range or in two groups, or too small a
+ * max_out_groups (the message gives the count needed).
+ */
+pa_status pa_shared_prefix_groups(const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t *context_lens, int32_t num_seqs,
+                                  const int32_t *group_offsets, int32_t num_groups,
+                                  const int32_t *group_seqs, int32_t block_size,
+                                  int32_t max_out_groups, int32_t *group_members,
+                                  int32_t *group_prefix, int32_t *seq_starts,
+                                  int32_t *num_out_groups, int32_t *max_prefix_len);
+
 #define PA_SHARED_OWN 1
 #define PA_SHARED_PREFIX 2
 #define PA_SHARED_COMBINE 4
@@ -418,7 +496,9 @@ pa_status pa_paged_attention_prefill_chunk(void *out, const void *q, const int32
  * PA_ERR_UNSUPPORTED otherwise.  Beyond pa_paged_attention_prefill_chunk's
  * preconditions: the blocks the chunk writes are not read by another
  * sequence of the batch, and key/value do not overlap the caches.  Under
- * PA_DEBUG_VALIDATE the checks of pa_paged_attention_prefill_chunk apply.
+ * PA_DEBUG_VALIDATE the checks of pa_paged_attention_prefill_chunk apply,
+ * and the written slots must be distinct and lie in blocks no other
+ * sequence of the batch reads.
  */
 pa_status pa_paged_attention_prefill_chunk_append(void *out, const void *q, const void *key,
                                                   const void *value, int64_t key_token_stride,

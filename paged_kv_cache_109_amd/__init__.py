@@ -2,8 +2,8 @@
 
 The computation lives in hand-written HIP kernels behind the C ABI of
 include/pagedattn.h (libpagedattn.so, built by `python
-paged_kv_cache_109_amd/build.py`); this package is the thin Python binding plus
-host-side slot translation. Importing it fails if the library is not built.
+paged_kv_cache_109_amd/build.py`); this package is the thin Python binding
+(argument marshalling only). Importing it fails if the library is not built.
 """
 from ._binding import (  # noqa: F401
     BlockManager,
@@ -34,8 +34,8 @@ from ._binding import (  # noqa: F401
     paged_attention_prefill_chunk,
     paged_attention_prefill_chunk_append,
     reshape_and_cache,
+    shared_prefix_groups,
+    slot_mapping,
     stream_read,
     swap_blocks,
 )
-from .sharing import shared_prefix_groups  # noqa: F401
-from .slots import slot_mapping  # noqa: F401

@@ -30,6 +30,8 @@ _SIGS = {
     "pa_abi_version": ([], ctypes.c_int),
     "pa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "pa_last_error": ([], ctypes.c_char_p),
+    "pa_slot_mapping": ([P, i32, i32, P, P, i64, i32, i64, P, P], ctypes.c_int),
+    "pa_shared_prefix_groups": ([P, i32, P, i32, P, i32, P, i32, i32, P, P, P, P, P], ctypes.c_int),
     "pa_reshape_and_cache": ([P, P, i64, i64, P, P, P, i64, i32, i32, i32, i64, ctypes.c_int, P], ctypes.c_int),
     "pa_decode_default_workers": ([ctypes.c_int, i32, i32], i32),
     "pa_decode_workspace_bytes": ([i32, i32, i32, i32, i32, i32], sz),
@@ -128,6 +130,30 @@ def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
     _contig(k_cache, "k_cache")
     _contig(v_cache, "v_cache")
     return tuple(int(x) for x in k_cache.shape)
+
+
+def slot_mapping(block_tables: torch.Tensor, seq_ids: torch.Tensor, positions: torch.Tensor, block_size: int,
+                 num_blocks: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Cache slot (int64, -1 for none) of each token (seq_ids[t], positions[t]),
+    translated on the device through block_tables (int32 [S, M]); seq_ids and
+    positions are int32 [T] device tensors. Returns `out` (allocated when
+    None)."""
+    _contig(block_tables, "block_tables")
+    _contig(seq_ids, "seq_ids")
+    _contig(positions, "positions")
+    if block_tables.dim() != 2 or seq_ids.dim() != 1 or positions.shape != seq_ids.shape:
+        raise ValueError("block_tables must be [num_seqs, max_blocks], seq_ids and positions [num_tokens]")
+    T = int(seq_ids.shape[0])
+    if out is None:
+        out = torch.empty(T, dtype=torch.int64, device=seq_ids.device)
+    _contig(out, "out")
+    if out.shape != (T,):
+        raise ValueError(f"out must be [{T}] int64")
+    _check(_lib.pa_slot_mapping(
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]), int(block_tables.shape[0]),
+        _dev(seq_ids, "seq_ids", torch.int32), _dev(positions, "positions", torch.int32), T, int(block_size),
+        int(num_blocks), _dev(out, "out", torch.int64), _stream(stream)), "slot_mapping")
+    return out
 
 
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -257,6 +283,38 @@ def paged_attention_decode_append_partitions(out, q, key, value, k_cache, v_cach
 
 MAX_GROUP_MEMBERS = 8
 SHARED_OWN, SHARED_PREFIX, SHARED_COMBINE, SHARED_ALL = 1, 2, 4, 7
+
+
+def shared_prefix_groups(block_tables, context_lens, groups: Sequence[Sequence[int]], block_size: int):
+    """The sharing description of paged_attention_decode_shared, derived by
+    the library (pa_shared_prefix_groups) from host block tables [S, M] and
+    context lengths [S] for the given groups of sequence ids. Returns numpy
+    (group_members int32 [G, 8], group_prefix int32 [G], seq_starts int32
+    [S], max_prefix_len)."""
+    import numpy as np
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if tables.ndim != 2 or lens.shape != (tables.shape[0],):
+        raise ValueError("block_tables must be [num_seqs, max_blocks] and context_lens [num_seqs]")
+    S = int(lens.shape[0])
+    members = [int(x) for g in groups for x in g]
+    offsets = np.zeros(len(groups) + 1, np.int32)
+    offsets[1:] = np.cumsum([len(g) for g in groups], dtype=np.int64)
+    flat = np.ascontiguousarray(members, dtype=np.int32)
+    cap = len(groups) + len(members) // MAX_GROUP_MEMBERS
+    gm = np.empty((max(cap, 1), MAX_GROUP_MEMBERS), np.int32)
+    gp = np.empty(max(cap, 1), np.int32)
+    starts = np.empty(max(S, 1), np.int32)
+    n_out, max_p = ctypes.c_int32(), ctypes.c_int32()
+    status = _lib.pa_shared_prefix_groups(
+        tables.ctypes.data, int(tables.shape[1]), lens.ctypes.data, S, offsets.ctypes.data, len(groups),
+        flat.ctypes.data if flat.size else None, int(block_size), cap, gm.ctypes.data, gp.ctypes.data,
+        starts.ctypes.data, ctypes.byref(n_out), ctypes.byref(max_p))
+    if status == PA_ERR_INVALID_ARG:
+        raise ValueError(_lib.pa_last_error().decode())
+    _check(status, "shared_prefix_groups")
+    n = n_out.value
+    return gm[:n].copy(), gp[:n].copy(), starts[:S].copy(), int(max_p.value)
 
 
 def alloc_decode_shared_workspace(num_seqs, num_heads, head_dim, max_context_len, block_size, num_groups,

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
-SOURCES = ["pa_api.cpp", "pa_block_manager.cpp", "pa_validate.cpp", "pa_decode.hip", "pa_shared.hip", "pa_cache.hip", "pa_prefill.hip", "pa_prefill_general.hip"]
+SOURCES = ["pa_api.cpp", "pa_block_manager.cpp", "pa_validate.cpp", "pa_sharing.cpp", "pa_decode.hip", "pa_shared.hip", "pa_cache.hip", "pa_prefill.hip", "pa_prefill_general.hip"]
 ARCH = "gfx950"
 
 

@@ -236,6 +236,22 @@ const char *pa_status_string(pa_status status) {
 
 const char *pa_last_error(void) { return g_last_error.c_str(); }
 
+pa_status pa_slot_mapping(const int32_t *block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                          const int32_t *seq_ids, const int32_t *positions, int64_t num_tokens, int32_t block_size,
+                          int64_t num_blocks, int64_t *slot_mapping, void *stream) {
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "sizes must be positive (num_tokens, num_seqs >= 0): num_tokens=%lld "
+                "num_seqs=%d max_blocks_per_seq=%d block_size=%d num_blocks=%lld", (long long)num_tokens, num_seqs,
+                max_blocks_per_seq, block_size, (long long)num_blocks);
+  if (num_tokens == 0) return ok();
+  if (!seq_ids || !positions || !slot_mapping || (num_seqs > 0 && !block_tables))
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  return hip_status(pa::launch_slot_mapping(block_tables, max_blocks_per_seq, num_seqs, seq_ids, positions,
+                                            num_tokens, block_size, num_blocks, slot_mapping,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                    "slot_mapping");
+}
+
 pa_status pa_reshape_and_cache(const void *key, const void *value, int64_t key_token_stride,
                                int64_t value_token_stride, void *k_cache, void *v_cache,
                                const int64_t *slot_mapping, int64_t num_tokens, int32_t num_heads,
@@ -333,7 +349,7 @@ static pa_status decode_impl(bool run_parts, bool run_reduce, void *out, const v
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (run_parts && pa::debug_validate()) {
     st = pa::validate_decode(block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs, block_size,
-                             num_blocks, s);
+                             num_blocks, app != nullptr, s);
     if (st != PA_OK) return st;
   }
   if (run_parts) {
@@ -616,7 +632,7 @@ static pa_status prefill_impl(void *out, const void *q, const int32_t *cu_q_lens
   if (pa::debug_validate()) {
     const pa_status vs = pa::validate_prefill(cu_q_lens, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                                               total_q, max_q_len, max_context_len, block_size, num_blocks,
-                                              reinterpret_cast<hipStream_t>(stream));
+                                              app != nullptr, reinterpret_cast<hipStream_t>(stream));
     if (vs != PA_OK) return vs;
   }
   return hip_status(pa::launch_prefill_chunk(a, dtype, head_dim, block_size, reinterpret_cast<hipStream_t>(stream)),

@@ -1,7 +1,9 @@
-// Cache write through a slot mapping, and batched whole-block copy.
+// Slot translation, cache write through a slot mapping, and batched
+// whole-block copy.
 //
-// Both are pure byte moves (no arithmetic, no conversion), so they are
-// bit-exact for every dtype.  Both are the fused single-launch kernels the
+// The write and the copies are pure byte moves (no arithmetic, no
+// conversion), so they are bit-exact for every dtype.  They are the fused
+// single-launch kernels the
 // Korean review of the vLLM paper (mz-moonzoo.tistory.com/116, section 5.1,
 // items 1 and 3) describes: the write replaces a split/reshape/scatter
 // sequence, and the copy replaces one small memcpy per block.
@@ -64,6 +66,47 @@ hipError_t launch_reshape_and_cache(const void *key, const void *value, int64_t 
   return hipSuccess;
 }
 
+// ------------------------------------------------------------- slot mapping
+//
+// Address translation of the tokens a step writes ("KV 캐시 관리와
+// PagedAttention", section on linking token order to storage): position p
+// of a sequence lies at offset p % B of its logical block p / B, which the
+// sequence's block table maps to a physical block; the flat slot is
+// physical * B + offset.  One lane per token; -1 marks a token that names no
+// valid slot (sequence or position out of range, table entry outside the
+// pool), which the cache write then skips.
+
+constexpr int kSlotMapGroups = 4096;
+
+__global__ __launch_bounds__(kCacheThreads) void slot_mapping_kernel(
+    const int32_t *__restrict__ block_tables, int32_t max_blocks, int32_t num_seqs,
+    const int32_t *__restrict__ seq_ids, const int32_t *__restrict__ positions, int64_t num_tokens,
+    int32_t block_size, int64_t num_blocks, int64_t *__restrict__ slot_mapping) {
+  for (int64_t t = (int64_t)blockIdx.x * kCacheThreads + threadIdx.x; t < num_tokens;
+       t += (int64_t)gridDim.x * kCacheThreads) {
+    const int32_t s = seq_ids[t], p = positions[t];
+    int64_t slot = -1;
+    if (s >= 0 && s < num_seqs && p >= 0) {
+      const int32_t logical = p / block_size;
+      if (logical < max_blocks) {
+        const int32_t phys = block_tables[(int64_t)s * max_blocks + logical];
+        if (phys >= 0 && phys < num_blocks) slot = (int64_t)phys * block_size + p % block_size;
+      }
+    }
+    slot_mapping[t] = slot;
+  }
+}
+
+hipError_t launch_slot_mapping(const int32_t *block_tables, int32_t max_blocks, int32_t num_seqs,
+                               const int32_t *seq_ids, const int32_t *positions, int64_t num_tokens,
+                               int32_t block_size, int64_t num_blocks, int64_t *slot_mapping, hipStream_t stream) {
+  const int64_t need = (num_tokens + kCacheThreads - 1) / kCacheThreads;
+  const unsigned groups = (unsigned)(need < kSlotMapGroups ? need : kSlotMapGroups);
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(groups), dim3(kCacheThreads), 0, stream, block_tables, max_blocks,
+                     num_seqs, seq_ids, positions, num_tokens, block_size, num_blocks, slot_mapping);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- copy_blocks
 
 struct LayerPtrs {
@@ -74,20 +117,11 @@ struct LayerPtrs {
 constexpr int kCopyUnroll = 4;
 constexpr int64_t kCopyChunk = (int64_t)kCacheThreads * 16 * kCopyUnroll;  // bytes per workgroup
 
-// grid.x = pair * chunks_per_block + chunk, grid.y = 2 * layer + (K=0 / V=1).
-__global__ __launch_bounds__(kCacheThreads) void copy_blocks_kernel(LayerPtrs ptrs,
-                                                                    const int64_t *__restrict__ mapping,
-                                                                    int64_t block_bytes, int64_t num_blocks,
-                                                                    int32_t chunks_per_block) {
-  const int64_t pair = blockIdx.x / chunks_per_block;
-  const int64_t chunk = blockIdx.x - pair * chunks_per_block;
-  const int layer = blockIdx.y >> 1;
-  char *base = (blockIdx.y & 1) ? ptrs.v[layer] : ptrs.k[layer];
-  const int64_t src = mapping[2 * pair];
-  const int64_t dst = mapping[2 * pair + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  const char *from = base + src * block_bytes;
-  char *to = base + dst * block_bytes;
+// One workgroup's part of a whole-block copy: chunk `chunk` (kCopyChunk
+// bytes) of the block_bytes at `from` onto `to`.  Each lane has all its
+// loads in flight before its first store.  Shared by the copy-on-write copy
+// within a pool and the swap between two pools.
+__device__ __forceinline__ void copy_block_chunk(const char *from, char *to, int64_t block_bytes, int64_t chunk) {
   const int64_t begin = chunk * kCopyChunk;
   uint4 r[kCopyUnroll];
   bool live[kCopyUnroll];
@@ -102,6 +136,21 @@ __global__ __launch_bounds__(kCacheThreads) void copy_blocks_kernel(LayerPtrs pt
     const int64_t o = begin + ((int64_t)u * kCacheThreads + threadIdx.x) * 16;
     if (live[u]) *reinterpret_cast<uint4 *>(to + o) = r[u];
   }
+}
+
+// grid.x = pair * chunks_per_block + chunk, grid.y = 2 * layer + (K=0 / V=1).
+__global__ __launch_bounds__(kCacheThreads) void copy_blocks_kernel(LayerPtrs ptrs,
+                                                                    const int64_t *__restrict__ mapping,
+                                                                    int64_t block_bytes, int64_t num_blocks,
+                                                                    int32_t chunks_per_block) {
+  const int64_t pair = blockIdx.x / chunks_per_block;
+  const int64_t chunk = blockIdx.x - pair * chunks_per_block;
+  const int layer = blockIdx.y >> 1;
+  char *base = (blockIdx.y & 1) ? ptrs.v[layer] : ptrs.k[layer];
+  const int64_t src = mapping[2 * pair];
+  const int64_t dst = mapping[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  copy_block_chunk(base + src * block_bytes, base + dst * block_bytes, block_bytes, chunk);
 }
 
 hipError_t launch_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t num_layers,
@@ -150,22 +199,8 @@ __global__ __launch_bounds__(kCacheThreads) void swap_blocks_kernel(SwapPtrs ptr
   const int64_t src = mapping[2 * pair];
   const int64_t dst = mapping[2 * pair + 1];
   if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
-  const char *from = ptrs.src[blockIdx.y] + src * block_bytes;
-  char *to = ptrs.dst[blockIdx.y] + dst * block_bytes;
-  const int64_t begin = chunk * kCopyChunk;
-  uint4 r[kCopyUnroll];
-  bool live[kCopyUnroll];
-#pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
-    const int64_t o = begin + ((int64_t)u * kCacheThreads + threadIdx.x) * 16;
-    live[u] = o < block_bytes;
-    if (live[u]) r[u] = *reinterpret_cast<const uint4 *>(from + o);
-  }
-#pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
-    const int64_t o = begin + ((int64_t)u * kCacheThreads + threadIdx.x) * 16;
-    if (live[u]) *reinterpret_cast<uint4 *>(to + o) = r[u];
-  }
+  copy_block_chunk(ptrs.src[blockIdx.y] + src * block_bytes, ptrs.dst[blockIdx.y] + dst * block_bytes, block_bytes,
+                   chunk);
 }
 
 hipError_t launch_swap_blocks(const void *const *src_caches, void *const *dst_caches, int32_t num_caches,

@@ -73,6 +73,10 @@ hipError_t launch_decode_reduce(const DecodeArgs &a, int dtype, int head_dim, hi
 // current device's copy, looked up once per device.
 hipError_t noalloc_scratch(void **ptr);
 
+hipError_t launch_slot_mapping(const int32_t *block_tables, int32_t max_blocks, int32_t num_seqs,
+                               const int32_t *seq_ids, const int32_t *positions, int64_t num_tokens,
+                               int32_t block_size, int64_t num_blocks, int64_t *slot_mapping, hipStream_t stream);
+
 hipError_t launch_reshape_and_cache(const void *key, const void *value, int64_t key_stride_bytes,
                                     int64_t value_stride_bytes, void *k_cache, void *v_cache,
                                     const int64_t *slot_mapping, int64_t num_tokens, int32_t num_heads,
@@ -168,13 +172,16 @@ hipError_t launch_prefill_general(const PrefillArgs &a, int dtype, int head_dim,
 // Debug validation of the data-dependent preconditions (pa_validate.cpp):
 // active when PA_DEBUG_VALIDATE=1; each synchronises `stream`, reads the
 // index arrays to the host and returns PA_ERR_INVALID_ARG (with the
-// last-error record set) at the first violation.
+// last-error record set) at the first violation.  `append`: the call also
+// writes each sequence's new tokens (fused decode append, fused chunk
+// write), whose slots must be distinct and in blocks no other sequence
+// reads.
 bool debug_validate();
 pa_status validate_slots(const int64_t *slot_mapping, int64_t num_tokens, int64_t num_blocks, int32_t block_size,
                          hipStream_t stream);
 pa_status validate_decode(const int32_t *block_tables, int32_t max_blocks, const int32_t *context_lens,
                           int32_t max_context_len, int32_t num_seqs, int32_t block_size, int64_t num_blocks,
-                          hipStream_t stream);
+                          bool append, hipStream_t stream);
 pa_status validate_shared(const int32_t *block_tables, int32_t max_blocks, const int32_t *context_lens,
                           int32_t max_context_len, int32_t num_seqs, int32_t block_size, int64_t num_blocks,
                           const int32_t *group_members, const int32_t *group_prefix, const int32_t *seq_starts,
@@ -184,7 +191,8 @@ pa_status validate_swap_pairs(const int64_t *block_mapping, int64_t num_pairs, i
                               int64_t dst_num_blocks, hipStream_t stream);
 pa_status validate_prefill(const int32_t *cu_q_lens, const int32_t *block_tables, int32_t max_blocks,
                            const int32_t *context_lens, int32_t num_seqs, int32_t total_q, int32_t max_q_len,
-                           int32_t max_context_len, int32_t block_size, int64_t num_blocks, hipStream_t stream);
+                           int32_t max_context_len, int32_t block_size, int64_t num_blocks, bool append,
+                           hipStream_t stream);
 hipError_t launch_prefill_chunk(const PrefillArgs &a, int dtype, int head_dim, int block_size,
                                 hipStream_t stream);
 

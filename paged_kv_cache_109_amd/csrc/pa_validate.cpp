@@ -8,15 +8,20 @@
 // block of the pool (the block table of "PagedAttention: Efficient Memory
 // Management for Large Language Model Serving", section 4.1), slots of one
 // write are distinct, a copy-on-write destination is a fresh block
-// ("KV 캐시 관리와 PagedAttention", copy-on-write section), and the sharing
-// description of a shared-prefix decode matches the tables.  The first
+// ("KV 캐시 관리와 PagedAttention", copy-on-write section), the sharing
+// description of a shared-prefix decode matches the tables, and the calls
+// that write the new tokens themselves write distinct slots of blocks no
+// other sequence reads.  The first
 // violation is reported through the last-error record.
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <algorithm>
+#include <unordered_map>
 #include <unordered_set>
+#include <utility>
 #include <vector>
 
 #include "pa_internal.h"
@@ -65,6 +70,42 @@ pa_status check_tables(const std::vector<int32_t> &tables, const std::vector<int
   return PA_OK;
 }
 
+// The fused-write calls store each sequence's new tokens themselves, at
+// positions [first[s], ctx[s]) (decode: the newest token only; prefill: the
+// chunk).  Their slots must be distinct, and no other sequence of the batch
+// may read a block being written: it would race with the store inside one
+// launch.  A block written to has one owner under copy-on-write ("KV 캐시
+// 관리와 PagedAttention", section on splitting a shared block that must be
+// written), so a shared block a caller forgot to copy is refused here.
+pa_status check_writes(const std::vector<int32_t> &tables, const std::vector<int32_t> &ctx,
+                       const std::vector<int32_t> &first, int32_t max_blocks, int32_t block_size) {
+  const size_t S = ctx.size();
+  // Up to two distinct readers of every block inside some context.
+  std::unordered_map<int32_t, std::pair<int32_t, int32_t>> readers;
+  for (size_t s = 0; s < S; ++s) {
+    const int64_t used = ((int64_t)ctx[s] + block_size - 1) / block_size;
+    for (int64_t b = 0; b < used; ++b) {
+      auto it = readers.emplace(tables[s * (size_t)max_blocks + b], std::make_pair((int32_t)s, -1)).first;
+      if (it->second.first != (int32_t)s && it->second.second < 0) it->second.second = (int32_t)s;
+    }
+  }
+  std::unordered_set<int64_t> written;
+  for (size_t s = 0; s < S; ++s) {
+    for (int32_t p = std::max(first[s], 0); p < ctx[s]; ++p) {
+      const int32_t blk = tables[s * (size_t)max_blocks + p / block_size];
+      const int64_t slot = (int64_t)blk * block_size + p % block_size;
+      if (!written.insert(slot).second)
+        return bad("slot " + str(slot) + " is written twice (sequence " + str(s) + ", position " + str(p) + ")");
+      const auto &r = readers.at(blk);
+      const int32_t other = r.first != (int32_t)s ? r.first : r.second;
+      if (other >= 0)
+        return bad("sequence " + str(s) + " writes position " + str(p) + " into block " + str(blk) +
+                   ", which sequence " + str(other) + " also reads (a shared block must be copied before a write)");
+    }
+  }
+  return PA_OK;
+}
+
 }  // namespace
 
 bool debug_validate() {
@@ -90,12 +131,16 @@ pa_status validate_slots(const int64_t *slot_mapping, int64_t num_tokens, int64_
 
 pa_status validate_decode(const int32_t *block_tables, int32_t max_blocks, const int32_t *context_lens,
                           int32_t max_context_len, int32_t num_seqs, int32_t block_size, int64_t num_blocks,
-                          hipStream_t stream) {
+                          bool append, hipStream_t stream) {
   std::vector<int32_t> tables, ctx;
   pa_status st = fetch(block_tables, (size_t)num_seqs * max_blocks, stream, tables, "block_tables");
   if (st == PA_OK) st = fetch(context_lens, (size_t)num_seqs, stream, ctx, "context_lens");
   if (st != PA_OK) return st;
-  return check_tables(tables, ctx, max_blocks, max_context_len, block_size, num_blocks);
+  st = check_tables(tables, ctx, max_blocks, max_context_len, block_size, num_blocks);
+  if (st != PA_OK || !append) return st;
+  std::vector<int32_t> first(ctx.size());
+  for (size_t s = 0; s < ctx.size(); ++s) first[s] = ctx[s] - 1;  // the newest token
+  return check_writes(tables, ctx, first, max_blocks, block_size);
 }
 
 pa_status validate_shared(const int32_t *block_tables, int32_t max_blocks, const int32_t *context_lens,
@@ -187,7 +232,8 @@ pa_status validate_swap_pairs(const int64_t *block_mapping, int64_t num_pairs, i
 
 pa_status validate_prefill(const int32_t *cu_q_lens, const int32_t *block_tables, int32_t max_blocks,
                            const int32_t *context_lens, int32_t num_seqs, int32_t total_q, int32_t max_q_len,
-                           int32_t max_context_len, int32_t block_size, int64_t num_blocks, hipStream_t stream) {
+                           int32_t max_context_len, int32_t block_size, int64_t num_blocks, bool append,
+                           hipStream_t stream) {
   std::vector<int32_t> cu, tables, ctx;
   pa_status st = fetch(cu_q_lens, (size_t)num_seqs + 1, stream, cu, "cu_q_lens");
   if (st == PA_OK) st = fetch(block_tables, (size_t)num_seqs * max_blocks, stream, tables, "block_tables");
@@ -204,7 +250,11 @@ pa_status validate_prefill(const int32_t *cu_q_lens, const int32_t *block_tables
       return bad("sequence " + str(s) + ": q_len " + str(q_len) + " exceeds context_lens = " + str(ctx[s]) +
                  " (the chunk is part of the context)");
   }
-  return check_tables(tables, ctx, max_blocks, max_context_len, block_size, num_blocks);
+  st = check_tables(tables, ctx, max_blocks, max_context_len, block_size, num_blocks);
+  if (st != PA_OK || !append) return st;
+  std::vector<int32_t> first(num_seqs);
+  for (int32_t s = 0; s < num_seqs; ++s) first[s] = ctx[s] - (cu[s + 1] - cu[s]);  // the chunk's first position
+  return check_writes(tables, ctx, first, max_blocks, block_size);
 }
 
 }  // namespace pa

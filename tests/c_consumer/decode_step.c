@@ -5,14 +5,16 @@
  *   decode_step check      host-side checks only (never touches a GPU):
  *                          version, status strings, an argument error.
  *   decode_step run DIR    one decode step from raw little-endian files in
- *                          DIR: the cache write of one new token per
- *                          sequence (pa_reshape_and_cache), then
+ *                          DIR: the slots of one new token per sequence
+ *                          (pa_slot_mapping), their cache write
+ *                          (pa_reshape_and_cache), then
  *                          pa_paged_attention_decode; writes DIR/out.bin,
- *                          DIR/k_out.bin and DIR/v_out.bin.
+ *                          DIR/k_out.bin, DIR/v_out.bin and DIR/slots.bin.
  *
  * DIR/meta.txt holds "S H D B N M max_ctx scale" (fp16 elements); the inputs
  * are q.bin [S][H][D], k.bin / v.bin [N][H][B][D], tables.bin int32 [S][M],
- * ctx.bin int32 [S], new_k.bin / new_v.bin [S][H][D], slots.bin int64 [S].
+ * ctx.bin int32 [S], new_k.bin / new_v.bin [S][H][D], seq.bin / pos.bin int32 [S]
+ * (sequence and position of each new token).
  * Exit status 0 on success; on failure the status and pa_last_error() are
  * printed.
  */
@@ -92,18 +94,25 @@ static int run(const char *dir) {
   void *hq = read_file(dir, "q.bin", qb), *hk = read_file(dir, "k.bin", cb), *hv = read_file(dir, "v.bin", cb);
   void *ht = read_file(dir, "tables.bin", (size_t)S * M * 4), *hc = read_file(dir, "ctx.bin", (size_t)S * 4);
   void *hnk = read_file(dir, "new_k.bin", qb), *hnv = read_file(dir, "new_v.bin", qb);
-  void *hs = read_file(dir, "slots.bin", (size_t)S * 8);
-  if (!hq || !hk || !hv || !ht || !hc || !hnk || !hnv || !hs) return fail("reading inputs", PA_ERR_INVALID_ARG);
+  void *hseq = read_file(dir, "seq.bin", (size_t)S * 4), *hpos = read_file(dir, "pos.bin", (size_t)S * 4);
+  if (!hq || !hk || !hv || !ht || !hc || !hnk || !hnv || !hseq || !hpos)
+    return fail("reading inputs", PA_ERR_INVALID_ARG);
 
   void *q = to_device(hq, qb), *k = to_device(hk, cb), *v = to_device(hv, cb);
   void *tables = to_device(ht, (size_t)S * M * 4), *ctx = to_device(hc, (size_t)S * 4);
-  void *nk = to_device(hnk, qb), *nv = to_device(hnv, qb), *slots = to_device(hs, (size_t)S * 8);
-  void *out = NULL;
-  if (!q || !k || !v || !tables || !ctx || !nk || !nv || !slots || hipMalloc(&out, qb) != hipSuccess)
+  void *nk = to_device(hnk, qb), *nv = to_device(hnv, qb);
+  void *seq = to_device(hseq, (size_t)S * 4), *pos = to_device(hpos, (size_t)S * 4);
+  void *out = NULL, *slots = NULL;
+  if (!q || !k || !v || !tables || !ctx || !nk || !nv || !seq || !pos || hipMalloc(&out, qb) != hipSuccess ||
+      hipMalloc(&slots, (size_t)S * 8) != hipSuccess)
     return fail("device buffers", PA_ERR_HIP);
 
-  /* The step: write the new tokens, then attend (the null stream). */
-  pa_status st = pa_reshape_and_cache(nk, nv, (int64_t)H * D, (int64_t)H * D, k, v, (const int64_t *)slots, S, H, D,
+  /* The step: translate the new tokens' positions to slots, write them,
+     then attend (the null stream). */
+  pa_status st = pa_slot_mapping((const int32_t *)tables, M, S, (const int32_t *)seq, (const int32_t *)pos, S, B, N,
+                                 (int64_t *)slots, NULL);
+  if (st != PA_OK) return fail("pa_slot_mapping", st);
+  st = pa_reshape_and_cache(nk, nv, (int64_t)H * D, (int64_t)H * D, k, v, (const int64_t *)slots, S, H, D,
                                       B, N, PA_F16, NULL);
   if (st != PA_OK) return fail("pa_reshape_and_cache", st);
   const size_t wsb = pa_decode_workspace_bytes(S, H, D, max_ctx, B, 0);
@@ -114,13 +123,15 @@ static int run(const char *dir) {
   if (st != PA_OK) return fail("pa_paged_attention_decode", st);
   if (hipDeviceSynchronize() != hipSuccess) return fail("hipDeviceSynchronize", PA_ERR_HIP);
 
-  void *hout = malloc(qb);
+  void *hout = malloc(qb), *hslots = malloc((size_t)S * 8);
   if (!hout || hipMemcpy(hout, out, qb, hipMemcpyDeviceToHost) != hipSuccess) return fail("copy out", PA_ERR_HIP);
+  if (!hslots || hipMemcpy(hslots, slots, (size_t)S * 8, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail("copy slots", PA_ERR_HIP);
   if (hipMemcpy(hk, k, cb, hipMemcpyDeviceToHost) != hipSuccess ||
       hipMemcpy(hv, v, cb, hipMemcpyDeviceToHost) != hipSuccess)
     return fail("copy caches", PA_ERR_HIP);
   if (write_file(dir, "out.bin", hout, qb) || write_file(dir, "k_out.bin", hk, cb) ||
-      write_file(dir, "v_out.bin", hv, cb))
+      write_file(dir, "v_out.bin", hv, cb) || write_file(dir, "slots.bin", hslots, (size_t)S * 8))
     return fail("writing outputs", PA_ERR_INVALID_ARG);
   printf("run ok: %d sequences, %d heads\n", S, H);
   return 0;

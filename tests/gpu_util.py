@@ -63,6 +63,15 @@ def check_attention(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str = 
     return max_abs, max_rel
 
 
+def device_slots(case, block_tables=None) -> torch.Tensor:
+    """Device int64 slot mapping of the case's new tokens, translated by the
+    library (pa_slot_mapping) through its block tables."""
+    import paged_kv_cache_109_amd as pa
+    bt = block_tables if block_tables is not None else dev(case.block_tables)
+    return pa.slot_mapping(bt, dev(np.asarray(case.new_seq, np.int32)), dev(np.asarray(case.new_pos, np.int32)),
+                           case.block_size, case.num_blocks)
+
+
 class DeviceCase:
     """A workloads.PagedCase with its tensors on the GPU."""
 

@@ -149,23 +149,3 @@ def test_rejects_bad_arguments_and_changes_nothing():
     with pytest.raises(pa.PagedAttnError):
         pa.BlockManager(3, 4, 2, free_order=[0, 0, 1])
     assert m.refcount(-1) == -1 and m.refcount(4) == -1
-
-
-def test_shared_prefix_groups_from_tables():
-    """The host description of sharing: P is the tokens of the leading
-    blocks every member shares and has filled, in whole 16-token tiles;
-    wide groups are split; sequences in no group start at 0."""
-    B = 16
-    tables = np.array([[5, 6, 7, -1], [5, 6, 9, -1], [5, 6, 7, 8], [1, 2, -1, -1], [3, -1, -1, -1]], np.int32)
-    lens = np.array([40, 33, 60, 20, 5], np.int32)
-    gm, gp, st, maxp = pa.shared_prefix_groups(tables, lens, [[0, 1, 2]], B)
-    assert gm.tolist() == [[0, 1, 2, -1, -1, -1, -1, -1]] and gp.tolist() == [32] and maxp == 32
-    assert st.tolist() == [32, 32, 32, 0, 0]
-    # The shared third block of 0 and 2 is not full in 0 (40 tokens): P stays 32.
-    _, gp, _, _ = pa.shared_prefix_groups(tables, lens, [[0, 2]], B)
-    assert gp.tolist() == [32]
-    wide = np.tile(np.array([[4, 5, 6, 7]], np.int32), (11, 1))
-    gm, gp, st, _ = pa.shared_prefix_groups(wide, np.full(11, 64, np.int32), [list(range(11))], B)
-    assert gm.shape == (2, 8) and gp.tolist() == [64, 64] and (st == 64).all()
-    with pytest.raises(ValueError):
-        pa.shared_prefix_groups(tables, lens, [[0, 1], [1, 2]], B)

@@ -3,10 +3,10 @@
 process (tests/c_consumer/decode_step.c).
 
 The CPU test compiles the consumer itself and runs its host-side checks.
-The GPU test runs the binary that build() made: one decode step (the cache
-write of one new token per sequence, then the decode) from raw files, whose
-written caches must equal the oracle's write bit for bit and whose output
-must match the oracle's decode.
+The GPU test runs the binary that build() made: one decode step (the slots
+of one new token per sequence, their cache write, then the decode) from raw
+files, whose slots and written caches must equal the oracle's bit for bit
+and whose output must match the oracle's decode.
 """
 import importlib.util
 import os
@@ -48,11 +48,12 @@ def test_decode_step_from_c_matches_the_oracle(tmp_path):
                                 f"{c.max_blocks_per_seq} {c.max_context_len} {c.scale!r}\n")
     for name, arr in (("q", c.q), ("k", c.k_cache), ("v", c.v_cache), ("tables", c.block_tables.astype(np.int32)),
                       ("ctx", c.context_lens.astype(np.int32)), ("new_k", c.new_key), ("new_v", c.new_value),
-                      ("slots", slots.astype(np.int64))):
+                      ("seq", c.new_seq.astype(np.int32)), ("pos", c.new_pos.astype(np.int32))):
         np.ascontiguousarray(arr).tofile(d / f"{name}.bin")
     say(f"  C consumer: {exe} run {d}")
     r = subprocess.run([exe, "run", str(d)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
+    assert np.array_equal(np.fromfile(d / "slots.bin", np.int64), slots)
     k_ref, v_ref = c.k_cache.copy(), c.v_cache.copy()
     oracle.reshape_and_cache(k_ref, v_ref, c.new_key, c.new_value, slots, "f16")
     assert np.fromfile(d / "k_out.bin", np.uint8).tobytes() == k_ref.tobytes()

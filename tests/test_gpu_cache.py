@@ -8,7 +8,7 @@ import torch
 import oracle
 import paged_kv_cache_109_amd as pa
 import workloads as W
-from gpu_util import DeviceCase, check_attention, dev, host, say
+from gpu_util import DeviceCase, check_attention, dev, device_slots, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -73,11 +73,11 @@ def test_large_batch_b256_full_size():
     """Write the 256 new tokens (position ctx-1) into the cache, then decode."""
     c = W.large_batch_b256()
     dc = DeviceCase(c)
-    slots = pa.slot_mapping(c.block_tables, c.new_seq, c.new_pos, c.block_size)
+    slots = device_slots(c, dc.block_tables)
     want_slots = oracle.slots(c.block_tables, c.new_seq, c.new_pos, c.block_size)
-    assert np.array_equal(slots, want_slots)
+    assert np.array_equal(slots.cpu().numpy(), want_slots)
     say(f"  large batch: reshape {len(slots)} tokens, then decode")
-    pa.reshape_and_cache(dev(c.new_key, c.dtype), dev(c.new_value, c.dtype), dc.k_cache, dc.v_cache, dev(slots))
+    pa.reshape_and_cache(dev(c.new_key, c.dtype), dev(c.new_value, c.dtype), dc.k_cache, dc.v_cache, slots)
     torch.cuda.synchronize()
     oracle.reshape_and_cache(c.k_cache, c.v_cache, c.new_key, c.new_value, want_slots, c.dtype)
     assert host(dc.k_cache, c.dtype).tobytes() == c.k_cache.tobytes()

@@ -14,7 +14,7 @@ import torch
 import oracle
 import paged_kv_cache_109_amd as pa
 import workloads as W
-from gpu_util import DeviceCase, check_attention, dev, say
+from gpu_util import DeviceCase, check_attention, dev, device_slots, say
 
 pytestmark = pytest.mark.gpu
 
@@ -38,12 +38,14 @@ def test_decode_step_graph_replays_match_eager():
     c = W.make_decode_case(8, 8, 128, 16, "f16", [5, 100, 700, 2048, 1, 33, 300, 1500], seed=11,
                            new_tokens=True, max_blocks_per_seq=128)
     dc = DeviceCase(c)
-    slots = dev(pa.slot_mapping(c.block_tables, c.new_seq, c.new_pos, c.block_size))
+    seq, pos = dev(np.asarray(c.new_seq, np.int32)), dev(np.asarray(c.new_pos, np.int32))
+    slots = torch.empty(c.num_seqs, dtype=torch.int64, device="cuda")
     nk, nv = dev(c.new_key, c.dtype), dev(c.new_value, c.dtype)
     ws = pa.alloc_decode_workspace(8, 8, 128, c.max_context_len, 16)
     out = torch.empty_like(dc.q)
 
-    def step():
+    def step():  # translation, cache write and decode, all on the device
+        pa.slot_mapping(dc.block_tables, seq, pos, c.block_size, c.num_blocks, out=slots)
         pa.reshape_and_cache(nk, nv, dc.k_cache, dc.v_cache, slots)
         pa.paged_attention_decode(out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
                                   c.max_context_len, c.scale, workspace=ws)
@@ -74,7 +76,7 @@ def test_decode_step_graph_replays_match_eager():
 def test_prefill_step_graph_replays_match_eager():
     c = W.make_prefill_case(3, 0, [0, 500, 1300], 4, 128, 16, "bf16", seed=5, q_lens=[100, 256, 37])
     dc = DeviceCase(c)
-    slots = dev(pa.slot_mapping(c.block_tables, c.new_seq, c.new_pos, c.block_size))
+    slots = device_slots(c)
     nk, nv = dev(c.new_key, c.dtype), dev(c.new_value, c.dtype)
     cu = dev(c.cu_q_lens)
     max_q = int(np.diff(c.cu_q_lens).max())

@@ -55,11 +55,19 @@ def check_case(c, what, **kw):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("B", [4, 16, 64])
+@pytest.mark.parametrize("B", [4, 8, 16, 32, 64])
 def test_prefill_append_shapes(dtype, B):
     c = W.make_prefill_case(4, 0, [0, 37, 700, 1500], 4, 128, B, dtype, seed=40 + B, q_lens=[1, 5, 130, 256],
                             name="append")
     check_case(c, f"{dtype} B={B}")
+
+
+def test_prefill_append_more_than_64_sequences():
+    # Past 64 sequences the kernel schedules the query tiles without ranking
+    # them by context length.
+    c = W.make_prefill_case(70, 0, lambda r, n: r.integers(0, 300, n), 2, 128, 16, "bf16", seed=49,
+                            q_lens=np.random.default_rng(50).integers(1, 40, 70), name="many")
+    check_case(c, "70 sequences")
 
 
 def test_prefill_append_three_query_tiles():

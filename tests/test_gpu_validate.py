@@ -216,6 +216,12 @@ def test_decode_append(validate):
             "block_tables[1][1]")
     refused(lambda: pa.paged_attention_decode_append(sentinel, q, nk, nv, k4, v4, bt, ctx, 63, c.scale),
             "context_lens[3] = 64")
+    # Copy-on-write forgotten: sequence 0 also reads the block that receives
+    # sequence 1's newest token (position 16, its second block).
+    shared = bt.clone()
+    shared[0, 1] = bt[1, 1]
+    refused(lambda: pa.paged_attention_decode_append(sentinel, q, nk, nv, k4, v4, shared, ctx, 64, c.scale),
+            "sequence 1 writes position 16 into block")
     torch.cuda.synchronize()
     assert bool((sentinel == 7.0).all()) and torch.equal(k4, k) and torch.equal(v4, v)
 
@@ -244,5 +250,23 @@ def test_prefill_chunk_append(validate):
     bad = bt.clone()
     bad[0, 2] = c.k_cache.shape[0]
     refused(lambda: call(sentinel, k3, v3, bt=bad), "block_tables[0][2]")
+    # Sequence 1 reads the block that receives sequence 0's chunk positions
+    # 30 and 31.
+    shared = bt.clone()
+    shared[1, 0] = bt[0, 1]
+    refused(lambda: call(sentinel, k3, v3, bt=shared), "sequence 0 writes position 30 into block")
     torch.cuda.synchronize()
     assert bool((sentinel == 7.0).all()) and torch.equal(k3, k) and torch.equal(v3, v)
+
+    # One sequence whose table names one block twice inside its chunk writes
+    # a slot twice.
+    c1 = W.make_prefill_case(1, 0, [0], 2, 128, 16, "bf16", seed=5, q_lens=[20], name="twice")
+    q1, k1, v1 = dev(c1.q, "bf16"), dev(c1.k_cache, "bf16"), dev(c1.v_cache, "bf16")
+    twice = dev(c1.block_tables)
+    twice[0, 1] = twice[0, 0]
+    sentinel1, kk, vv = torch.full_like(q1, 7.0), k1.clone(), v1.clone()
+    refused(lambda: pa.paged_attention_prefill_chunk_append(
+        sentinel1, q1, dev(c1.new_key, "bf16"), dev(c1.new_value, "bf16"), dev(c1.cu_q_lens), kk, vv, twice,
+        dev(c1.context_lens), 20, 20, c1.scale), "is written twice (sequence 0, position 16)")
+    torch.cuda.synchronize()
+    assert bool((sentinel1 == 7.0).all()) and torch.equal(kk, k1) and torch.equal(vv, v1)
