@@ -1,6 +1,6 @@
 """Benchmark of the paged decode-attention step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload opt13b_b64]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|opt13b_b64|...]
 
 A step is one decode iteration of the hot path over one batch (the loop the
 Korean review of the vLLM paper, mz-moonzoo.tistory.com/116, section 4.3,
@@ -18,10 +18,16 @@ pass with one new token per sequence, or the chunked prefill kernel) instead
 of launching reshape_and_cache first; the default keeps the two launches.
 
 Prints ONE JSON line. `value` is decode tokens/s for one layer call (one
-query token per sequence per step). `roofline` is for the dominant kernel,
-the decode partition pass, whose launches are bracketed by HIP events on the
-stream they run on, in a separate eager pass. `cpu_baseline` times the CPU oracle (test
-infrastructure, never tuned) on the same batch on the host cores.
+query token per sequence per step) on opt13b_b64 (64 sequences, OPT-13B
+layer shapes); `per_model_step` divides it over OPT-13B's 40 layers.
+`roofline` is for the dominant kernel, the decode partition pass, whose
+launches are bracketed by HIP events on the stream they run on, in a
+separate eager pass. `cpu_baseline` times the CPU oracle (test
+infrastructure, never tuned) on the same batch on the host cores. With the
+default --workload all, `workloads` holds the same figures for the other
+workloads -- large_batch_b256, parallel_sampling (plain and shared-prefix
+steps, the 40-layer copy-on-write copy, swaps) and chunked_prefill (with the
+MFMA fraction) -- each with its own roofline and a shorter oracle sample.
 """
 from __future__ import annotations
 
@@ -40,6 +46,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak
 METRIC = "paged decode attn tokens/s + effective KV GB/s (% HBM peak), OPT-13B shapes"
+MODEL_LAYERS = 40  # OPT-13B: one decode step of the model is 40 layer calls
 
 
 def parse():
@@ -47,7 +54,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="opt13b_b64", choices=["opt13b_b64", "large_batch_b256", "parallel_sampling", "chunked_prefill"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "opt13b_b64", "large_batch_b256", "parallel_sampling", "chunked_prefill"],
+                    help="all: opt13b_b64 as the headline line, the others under its `workloads` key")
     ap.add_argument("--replicas", type=int, default=2,
                     help="copies of the KV pool used in turn, so no step finds the last one's data in cache")
     ap.add_argument("--split-workers", type=int, default=0,
@@ -67,6 +76,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU oracle on the batch until this much time has passed (at least 3 runs)")
+    ap.add_argument("--cpu-seconds-others", type=float, default=4.0,
+                    help="the same for the other workloads of --workload all")
     return ap.parse_args()
 
 
@@ -91,6 +102,10 @@ def committed_traffic(profile: str, source: str = "pa_decode.hip"):
               f"({m.group(1) if m else '?'} vs {kernel_source_digest(source)}): traffic = null", file=sys.stderr)
         return None
     return float(t.group(1))
+
+
+def traffic_source(profile: str) -> str:
+    return f"profiles/{profile}_counters.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated; taken on this kernel source)"
 
 
 def calibrate_counters(torch, dev):
@@ -207,26 +222,72 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    import torch
+
+    import paged_kv_cache_109_amd as pa
+
+    if args.workload == "all" and (args.num_seqs is not None or args.dtype or args.block_size != 16):
+        print("--num-seqs, --dtype and --block-size apply to a single --workload", file=sys.stderr)
+        sys.exit(2)
+    if args.workload == "chunked_prefill" and args.block_size != 16:
+        print("the chunked_prefill workload uses 16-token blocks", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    calibrate_counters(torch, dev)
+    stream_read = measure_stream_read(torch, pa, dev)
+    if args.workload == "chunked_prefill":
+        result = run_prefill(args, stream_read, args.cpu_seconds)
+    else:
+        first = "opt13b_b64" if args.workload == "all" else args.workload
+        result = run_decode(first, args, stream_read, args.cpu_seconds)
+    if args.workload == "all":
+        others = {}
+        for name in ("large_batch_b256", "parallel_sampling", "chunked_prefill"):
+            torch.cuda.empty_cache()
+            line = (run_prefill(args, stream_read, args.cpu_seconds_others) if name == "chunked_prefill"
+                    else run_decode(name, args, stream_read, args.cpu_seconds_others))
+            for k in ("n_gpus", "steps", "warmup", "higher_is_better", "scaling", "data", "stream_read"):
+                line.pop(k, None)
+            others[name] = line
+        result["workloads"] = others
+    print(json.dumps(result))
+
+
+def oracle_baseline(fn, seconds: float, units: int, unit: str, what: str, kv_bytes: int = 0):
+    """The CPU oracle (test infrastructure, never tuned) repeated on a batch
+    for about `seconds` on every host core this process may use."""
+    import numpy as np
+    import oracle
+    oracle.load()
+    threads = len(os.sched_getaffinity(0))
+    times = time_oracle(lambda: fn(threads), seconds)
+    t_med = float(np.median(times))
+    cpu = {"value": units / t_med, "unit": unit, "cores": threads, "kind": "oracle",
+           "sample": f"{what} {len(times)} times ({sum(times):.1f}s) by the fp64 C oracle with OpenMP; median "
+                     f"{t_med:.2f}s per batch; CPU {cpu_model()}"}
+    if kv_bytes:
+        cpu["effective_kv_gbps"] = kv_bytes / t_med / 1e9
+    return cpu
+
+
+def run_decode(name, args, stream_read, cpu_seconds):
+    """One decode workload: the timed step, the partition pass's roofline,
+    the other kernels of the step, and the oracle baseline."""
     import numpy as np
     import torch
 
     import paged_kv_cache_109_amd as pa
     import workloads as W
 
-    if args.workload == "chunked_prefill":
-        if args.block_size != 16:
-            print("the chunked_prefill workload uses 16-token blocks", file=sys.stderr)
-            sys.exit(2)
-        return bench_prefill(args)
     t0 = time.time()
     extra = {"dtype": args.dtype} if args.dtype else {}
     if args.num_seqs is not None:
-        if args.workload not in ("opt13b_b64", "large_batch_b256") or args.num_seqs < 1:
+        if name not in ("opt13b_b64", "large_batch_b256") or args.num_seqs < 1:
             print("--num-seqs applies to the opt13b_b64 and large_batch_b256 workloads (>= 1)", file=sys.stderr)
             sys.exit(2)
         extra["num_seqs"] = args.num_seqs
     case = {"opt13b_b64": W.opt13b_b64, "large_batch_b256": W.large_batch_b256,
-            "parallel_sampling": W.parallel_sampling}[args.workload](block_size=args.block_size, **extra)
+            "parallel_sampling": W.parallel_sampling}[name](block_size=args.block_size, **extra)
     print(f"[bench] workload {case.name} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
@@ -259,9 +320,6 @@ def main():
     workers = args.split_workers
     ws = pa.alloc_decode_workspace(S, H, D, max_ctx, B, workers, device=dev)
     stream = torch.cuda.current_stream()
-
-    calibrate_counters(torch, dev)
-    stream_read = measure_stream_read(torch, pa, dev)
 
     def step(i, ev=None):
         # ev: four events on the launch stream -- step start, after the cache
@@ -418,18 +476,14 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        oracle.load()
-        threads = len(os.sched_getaffinity(0))
-        times = time_oracle(lambda: oracle.decode(case.q, case.k_cache, case.v_cache, case.block_tables,
-                                                  case.context_lens, case.scale, case.dtype, threads=threads),
-                            args.cpu_seconds)
-        t_med = float(np.median(times))
-        cpu = {"value": S / t_med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": f"the whole {case.name} batch ({S} seqs, {int(case.context_lens.sum())} context tokens, "
-                         f"{H} heads) decoded {len(times)} times ({sum(times):.1f}s) by the fp64 C oracle with "
-                         f"OpenMP over (seq, head); median {t_med:.2f}s per batch; CPU {cpu_model()}",
-               "effective_kv_gbps": kv_bytes / t_med / 1e9}
+        cpu = oracle_baseline(
+            lambda th: oracle.decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens,
+                                     case.scale, case.dtype, threads=th),
+            cpu_seconds, S, "tokens/s",
+            f"the whole {case.name} batch ({S} seqs, {int(case.context_lens.sum())} context tokens, {H} heads) "
+            f"decoded", kv_bytes)
 
+    traffic_profile = ("decode_partition_" + ("append_" if fused else "") + case.name.rsplit("_", 1)[0])
     result = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -450,6 +504,9 @@ def main():
                    "step": ("copy_blocks(CoW pairs) + " if copies else "")
                    + ("decode partitions with the new tokens' cache write fused in + decode reduce" if fused else
                       ("reshape_and_cache(new tokens) + " if writes else "") + "decode partitions + decode reduce")},
+        "per_model_step": {"layers": MODEL_LAYERS, "tokens_per_s": tokens_per_s / MODEL_LAYERS,
+                           "ms_per_model_step": ms_per_step * MODEL_LAYERS,
+                           "note": "one layer call per step timed; a model step is 40 of them (OPT-13B)"},
         "effective_kv_gbps": kv_bytes / (ms_per_step * 1e-3) / 1e9,
         "pct_hbm_peak": kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "stream_read": stream_read,
@@ -457,7 +514,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel" + (" (append)" if fused else ""),
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic, "alg_bytes_per_launch": alg_bytes, "avg_launch_us": part_avg_s * 1e6,
+                     "traffic": traffic, "traffic_source": traffic_source(traffic_profile) if traffic else None,
+                     "alg_bytes_per_launch": alg_bytes, "avg_launch_us": part_avg_s * 1e6,
                      **launch_stats(part_ms), "frac_of_stream_read": achieved / stream_read["gbps"]},
         "components": components,
         "cpu_baseline": cpu,
@@ -466,10 +524,10 @@ def main():
         shared = sorted({b for blocks in case.seq_blocks for b in blocks})
         result["config"]["distinct_blocks_read"] = len(shared)
         result["config"]["distinct_block_bytes"] = len(shared) * 2 * row * B
-    print(json.dumps(result))
+    return result
 
 
-def bench_prefill(args):
+def run_prefill(args, stream_read, cpu_seconds):
     """Chunked prefill (16 x 256-query causal chunks, bf16): a step writes the
     chunk's K/V (reshape_and_cache, 4096 tokens) and runs the MFMA kernel."""
     import numpy as np
@@ -498,8 +556,6 @@ def bench_prefill(args):
     q_lens = np.diff(case.cu_q_lens)
     max_q, max_ctx = int(q_lens.max()), case.max_context_len
     stream = torch.cuda.current_stream()
-    calibrate_counters(torch, dev)
-    stream_read = measure_stream_read(torch, pa, dev)
 
     fused = args.step == "fused"
 
@@ -542,15 +598,13 @@ def bench_prefill(args):
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        threads = len(os.sched_getaffinity(0))
-        times = time_oracle(lambda: oracle.prefill_chunk(case.q, case.cu_q_lens, case.k_cache, case.v_cache,
-                                                         case.block_tables, case.context_lens, case.scale,
-                                                         case.dtype, threads=threads), args.cpu_seconds)
-        dt_cpu = float(np.median(times))
-        cpu = {"value": int(q_lens.sum()) / dt_cpu, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
-               "sample": f"the whole chunked_prefill batch ({S} x {max_q} queries, {H} heads) {len(times)} times "
-                         f"({sum(times):.1f}s) by the fp64 C oracle with OpenMP; median {dt_cpu:.2f}s per batch; "
-                         f"CPU {cpu_model()}"}
+        cpu = oracle_baseline(
+            lambda th: oracle.prefill_chunk(case.q, case.cu_q_lens, case.k_cache, case.v_cache, case.block_tables,
+                                            case.context_lens, case.scale, case.dtype, threads=th),
+            cpu_seconds, int(q_lens.sum()), "query tokens/s",
+            f"the whole chunked_prefill batch ({S} x {max_q} queries, {H} heads)")
+    profile = "prefill_chunk_" + ("append_" if fused else "") + "chunked_prefill"
+    traffic = committed_traffic(profile, "pa_prefill.hip")
     result = {
         "metric": "chunked prefill paged attention query tokens/s (MFMA), OPT-13B shapes",
         "value": int(q_lens.sum()) / (ms_per_step * 1e-3), "unit": "query tokens/s", "n_gpus": 1,
@@ -564,17 +618,19 @@ def bench_prefill(args):
         "stream_read": stream_read,
         "roofline": {"bound": "hbm", "kernel": "prefill_chunk_kernel" + (" (append)" if fused else ""),
                      "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
-                     "traffic": committed_traffic("prefill_chunk_" + ("append_" if fused else "") + "chunked_prefill",
-                                                  "pa_prefill.hip"),
+                     "traffic": traffic,
+                     "traffic_source": traffic_source(profile) if traffic else None,
                      "alg_bytes_per_launch": kv_bytes + qo_bytes + write_bytes, "avg_launch_us": kern_s * 1e6,
                      **launch_stats(kern_ms), "frac_of_stream_read": gbps / stream_read["gbps"],
                      "mfma_tflops": tflops, "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                      "mfma_frac": tflops / MFMA_BF16_PEAK_TFLOPS, "causal_flops_per_launch": flops},
         "cpu_baseline": cpu,
     }
+    result["per_model_step"] = {"layers": MODEL_LAYERS, "query_tokens_per_s": result["value"] / MODEL_LAYERS,
+                                "ms_per_model_step": ms_per_step * MODEL_LAYERS}
     print(f"[bench] prefill step {ms_per_step * 1e3:.1f} us; kernel {kern_s * 1e6:.1f} us; {tflops:.0f} TFLOP/s; "
           f"{gbps:.0f} GB/s", file=sys.stderr, flush=True)
-    print(json.dumps(result))
+    return result
 
 
 if __name__ == "__main__":
