@@ -13,9 +13,13 @@ The timed steps are eager launches of the step's kernels with nothing else
 between the two events that bracket them. --graph replays the step captured
 once as a HIP graph instead (one graph per pool replica: the same kernels on
 the same buffers); on ROCm 7 that measured slower than eager launches.
---step fused folds the cache write into the attention kernel (the decode
-pass with one new token per sequence, or the chunked prefill kernel) instead
-of launching reshape_and_cache first; the default keeps the two launches.
+By default (--step fused) a decode step with one new token per sequence is
+two launches: the partition pass reads each sequence's newest token from its
+new K/V rows, and the reduce pass stores those rows into the cache after
+every read (paged_attention_decode_append); --step separate launches
+reshape_and_cache first, then the plain passes. --prefill-step fused runs the
+chunked prefill with its fused-write kernel instead of reshape_and_cache
+first.
 
 Prints ONE JSON line. `value` is decode tokens/s for one layer call (one
 query token per sequence per step) on opt13b_b64 (64 sequences, OPT-13B
@@ -70,9 +74,13 @@ def parse():
                     help="tokens per KV block for the decode workloads (4, 8, 16, 32 or 64)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the step captured as a HIP graph instead of eager launches")
-    ap.add_argument("--step", default="separate", choices=["fused", "separate"],
-                    help="decode workloads with one new token per sequence: write it inside the partition pass "
-                         "(fused, paged_attention_decode_append) or with reshape_and_cache first (separate)")
+    ap.add_argument("--step", default="fused", choices=["fused", "separate"],
+                    help="decode workloads with one new token per sequence: the partition pass reads the new "
+                         "token from its rows and the reduce pass stores it (fused, paged_attention_decode_append: "
+                         "two launches), or reshape_and_cache first (separate: three launches)")
+    ap.add_argument("--prefill-step", default="separate", choices=["fused", "separate"],
+                    help="chunked_prefill: the fused-write kernel (the chunk's K/V stored by the prefill kernel) or "
+                         "reshape_and_cache first")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU oracle on the batch until this much time has passed (at least 3 runs)")
@@ -342,8 +350,13 @@ def run_decode(name, args, stream_read, cpu_seconds):
                                                  case.scale, workspace=ws, split_workers=workers)
         if ev is not None:
             ev[2].record(stream)
-        pa.paged_attention_decode_reduce(out, context_lens, max_ctx, case.max_blocks_per_seq, H, D, B,
-                                         workspace=ws, split_workers=workers)
+        if fused:
+            pa.paged_attention_decode_append_reduce(out, q, new_k, new_v, k_cache, v_cache, block_tables,
+                                                    context_lens, max_ctx, case.scale, workspace=ws,
+                                                    split_workers=workers)
+        else:
+            pa.paged_attention_decode_reduce(out, context_lens, max_ctx, case.max_blocks_per_seq, H, D, B,
+                                             workspace=ws, split_workers=workers)
         if ev is not None:
             ev[3].record(stream)
 
@@ -557,7 +570,7 @@ def run_prefill(args, stream_read, cpu_seconds):
     max_q, max_ctx = int(q_lens.max()), case.max_context_len
     stream = torch.cuda.current_stream()
 
-    fused = args.step == "fused"
+    fused = args.prefill_step == "fused"
 
     def step(i, ev=None):
         k_cache, v_cache = pools[i % len(pools)]

@@ -237,13 +237,14 @@ pa_status pa_paged_attention_decode_noalloc(void *out, const void *q, const void
 
 /*
  * pa_paged_attention_decode_append -- the decode step's cache write and its
- * attention in one pass.  A decode step first stores the new token's K and V
- * in its slot, then attends over a context that includes it ("KV 캐시 관리와
- * PagedAttention", section on attention over scattered KV).  The pages fuse
- * the write's steps into one kernel to save launches (review section 5.1,
- * item 1; notes section 4.1); this call goes one launch further: the
- * partition pass reads the newest token from key/value and writes it into
- * the cache itself.
+ * attention in two launches instead of three.  A decode step first stores
+ * the new token's K and V in its slot, then attends over a context that
+ * includes it ("KV 캐시 관리와 PagedAttention", section on attention over
+ * scattered KV).  The pages fuse the write's steps into one kernel to save
+ * launches (review section 5.1, item 1; notes section 4.1); this call goes
+ * one launch further: the partition pass reads the newest token from
+ * key/value instead of the cache, and the reduce pass, which runs after
+ * every read of the partition pass, stores it into the cache.
  *
  * For each sequence s with n = context_lens[s] >= 1 (clipped to
  * max_context_len as in pa_paged_attention_decode), key[s] and value[s]
@@ -280,10 +281,21 @@ pa_status pa_paged_attention_decode_append(void *out, const void *q, const void 
                                            pa_dtype dtype, int32_t split_workers, void *workspace,
                                            size_t workspace_bytes, void *stream);
 
-/* The partition pass of pa_paged_attention_decode_append alone (same
- * arguments), cache write included; pa_paged_attention_decode_reduce then
- * finishes it exactly as it finishes pa_paged_attention_decode_partitions. */
+/* The two passes of pa_paged_attention_decode_append, separately (same
+ * arguments each).  The partition pass reads the newest tokens from
+ * key/value and writes nothing to the caches;
+ * pa_paged_attention_decode_append_reduce then merges the cut pairs into
+ * `out` and stores the newest tokens into the caches.  Together they leave
+ * the same bytes as pa_paged_attention_decode_append; between the two calls
+ * the caches do not yet hold the new tokens. */
 pa_status pa_paged_attention_decode_append_partitions(
+    void *out, const void *q, const void *key, const void *value, int64_t key_seq_stride,
+    int64_t value_seq_stride, void *k_cache, void *v_cache, const int32_t *block_tables,
+    int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+    int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+    float scale, pa_dtype dtype, int32_t split_workers, void *workspace, size_t workspace_bytes,
+    void *stream);
+pa_status pa_paged_attention_decode_append_reduce(
     void *out, const void *q, const void *key, const void *value, int64_t key_seq_stride,
     int64_t value_seq_stride, void *k_cache, void *v_cache, const int32_t *block_tables,
     int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,

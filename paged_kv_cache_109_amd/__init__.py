@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     paged_attention_decode,
     paged_attention_decode_append,
     paged_attention_decode_append_partitions,
+    paged_attention_decode_append_reduce,
     paged_attention_decode_noalloc,
     NOALLOC_SCRATCH_BYTES,
     paged_attention_decode_partitions,

@@ -47,6 +47,9 @@ _SIGS = {
     "pa_paged_attention_decode_append_partitions": (
         [P, P, P, P, i64, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, i32, P, sz, P],
         ctypes.c_int),
+    "pa_paged_attention_decode_append_reduce": (
+        [P, P, P, P, i64, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, i32, P, sz, P],
+        ctypes.c_int),
     "pa_paged_attention_decode_reduce": (
         [P, P, i32, i32, i32, i32, i32, i32, ctypes.c_int, i32, P, sz, P], ctypes.c_int),
     "pa_copy_blocks": ([P, P, i32, P, i64, i64, i64, P], ctypes.c_int),
@@ -279,6 +282,17 @@ def paged_attention_decode_append_partitions(out, q, key, value, k_cache, v_cach
     _check(_lib.pa_paged_attention_decode_append_partitions(*_append_args(
         out, q, key, value, k_cache, v_cache, block_tables, context_lens, max_context_len, scale, split_workers,
         workspace, stream)), "paged_attention_decode_append_partitions")
+
+
+def paged_attention_decode_append_reduce(out, q, key, value, k_cache, v_cache, block_tables, context_lens,
+                                         max_context_len, scale, workspace=None, split_workers=0,
+                                         stream=None) -> None:
+    """Second pass of paged_attention_decode_append: merges the cut pairs the
+    append partition pass left and stores the newest tokens' rows into the
+    caches."""
+    _check(_lib.pa_paged_attention_decode_append_reduce(*_append_args(
+        out, q, key, value, k_cache, v_cache, block_tables, context_lens, max_context_len, scale, split_workers,
+        workspace, stream)), "paged_attention_decode_append_reduce")
 
 
 MAX_GROUP_MEMBERS = 8

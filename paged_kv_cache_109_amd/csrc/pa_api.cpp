@@ -135,8 +135,9 @@ pa_status check_decode_common(const void *k_cache, const void *v_cache, const in
 
 pa::DecodeArgs decode_args(void *out, const void *q, const void *k_cache, const void *v_cache,
                            const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
-                           int32_t num_seqs, int32_t num_heads, int32_t head_dim, pa_dtype dtype,
-                           int64_t num_blocks, float scale, const DecodeGeometry &g, const void *workspace) {
+                           int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                           pa_dtype dtype, int64_t num_blocks, float scale, const DecodeGeometry &g,
+                           const void *workspace) {
   pa::DecodeArgs a;
   char *ws = reinterpret_cast<char *>(const_cast<void *>(workspace));
   a.out = out;
@@ -151,6 +152,7 @@ pa::DecodeArgs decode_args(void *out, const void *q, const void *k_cache, const 
   a.num_seqs = num_seqs;
   a.max_blocks = max_blocks_per_seq;
   a.num_heads = num_heads;
+  a.block_size = block_size;
   a.ctx_cap = g.ctx_cap;
   a.workers = (int32_t)g.workers;
   a.out_row_words = (int32_t)((int64_t)num_heads * head_dim * elt_bytes(dtype) / 4);
@@ -266,8 +268,9 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, int64_t key_t
     return fail(PA_ERR_UNSUPPORTED, "head_dim * element size (%lld bytes) must be a multiple of 16",
                 (long long)row_bytes);
   if (row_bytes > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "head_dim too large");
-  if (2 * (int64_t)num_heads * (row_bytes / 16) > 0x7fffffff)
-    return fail(PA_ERR_UNSUPPORTED, "num_heads * head_dim too large (a token's K and V exceed 2^31 16-byte chunks)");
+  if (2 * (int64_t)num_heads * (row_bytes / 16) > 65535LL * 256)
+    return fail(PA_ERR_UNSUPPORTED, "num_heads * head_dim too large (a token's K and V exceed 65535 * 256 16-byte "
+                "chunks)");
   if (key_token_stride < (int64_t)num_heads * head_dim || value_token_stride < (int64_t)num_heads * head_dim)
     return fail(PA_ERR_INVALID_ARG, "token strides (%lld, %lld) smaller than num_heads*head_dim %lld",
                 (long long)key_token_stride, (long long)value_token_stride, (long long)num_heads * head_dim);
@@ -339,7 +342,7 @@ static pa_status decode_impl(bool run_parts, bool run_reduce, void *out, const v
   st = check_workspace(g, workspace, workspace_bytes);
   if (st != PA_OK) return st;
   pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
-                                 num_seqs, num_heads, head_dim, dtype, num_blocks, scale, g, workspace);
+                                 num_seqs, num_heads, head_dim, block_size, dtype, num_blocks, scale, g, workspace);
   if (app) {
     a.new_key = app->key;
     a.new_value = app->value;
@@ -347,7 +350,7 @@ static pa_status decode_impl(bool run_parts, bool run_reduce, void *out, const v
     a.new_value_stride = app->value_stride * elt_bytes(dtype);
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (run_parts && pa::debug_validate()) {
+  if ((run_parts || app) && pa::debug_validate()) {
     st = pa::validate_decode(block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs, block_size,
                              num_blocks, app != nullptr, s);
     if (st != PA_OK) return st;
@@ -426,6 +429,18 @@ pa_status pa_paged_attention_decode_append_partitions(
                      split_workers, workspace, workspace_bytes, stream, &app);
 }
 
+pa_status pa_paged_attention_decode_append_reduce(
+    void *out, const void *q, const void *key, const void *value, int64_t key_seq_stride, int64_t value_seq_stride,
+    void *k_cache, void *v_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+    const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+    int32_t block_size, int64_t num_blocks, float scale, pa_dtype dtype, int32_t split_workers, void *workspace,
+    size_t workspace_bytes, void *stream) {
+  const AppendRows app{key, value, key_seq_stride, value_seq_stride};
+  return decode_impl(false, true, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks, scale, dtype,
+                     split_workers, workspace, workspace_bytes, stream, &app);
+}
+
 pa_status pa_paged_attention_decode_partitions(void *out, const void *q, const void *k_cache, const void *v_cache,
                                                const int32_t *block_tables, int32_t max_blocks_per_seq,
                                                const int32_t *context_lens, int32_t max_context_len,
@@ -458,7 +473,7 @@ pa_status pa_paged_attention_decode_reduce(void *out, const int32_t *context_len
   if (!out || !context_lens) return fail(PA_ERR_INVALID_ARG, "null out or context-length pointer");
   if (!aligned16(out)) return fail(PA_ERR_INVALID_ARG, "out must be 16-byte aligned");
   const pa::DecodeArgs a = decode_args(out, nullptr, nullptr, nullptr, nullptr, max_blocks_per_seq, context_lens,
-                                       num_seqs, num_heads, head_dim, dtype, 1, 1.f, g, workspace);
+                                       num_seqs, num_heads, head_dim, block_size, dtype, 1, 1.f, g, workspace);
   return hip_status(pa::launch_decode_reduce(a, dtype, head_dim, reinterpret_cast<hipStream_t>(stream)),
                     "decode reduce");
 }
@@ -507,7 +522,7 @@ pa_status pa_paged_attention_decode_shared(void *out, const void *q, const void 
   if (!aligned16(workspace)) return fail(PA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   char *ws = reinterpret_cast<char *>(workspace);
   pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                                 num_heads, head_dim, dtype, num_blocks, scale, g.dec, workspace);
+                                 num_heads, head_dim, block_size, dtype, num_blocks, scale, g.dec, workspace);
   a.starts = seq_starts;
   a.suffix_out = reinterpret_cast<float *>(ws + g.suffix_off);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

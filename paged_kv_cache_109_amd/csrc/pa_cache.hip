@@ -20,30 +20,34 @@ namespace pa {
 
 constexpr int kCacheThreads = 256;
 
-// One workgroup per new token: copy its num_heads K rows and V rows into
-// (slot / B, h, slot % B).  Rows are row_bytes long, a multiple of 16.
+// Grid (token, part): workgroup (t, y) copies 16-byte chunks y*256 ..
+// y*256+255 of token t's K rows then V rows (num_heads rows of row_bytes
+// each, a multiple of 16) into (slot / B, h, slot % B).  Each lane moves at
+// most one chunk, so a token's copy is one load and one store deep however
+// many heads it has, and a batch of a few tokens still spreads over many
+// workgroups; the slot is read once per workgroup, as a scalar load.
 __global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(
     const char *__restrict__ key, const char *__restrict__ value, int64_t key_stride_bytes,
     int64_t value_stride_bytes, char *__restrict__ k_cache, char *__restrict__ v_cache,
     const int64_t *__restrict__ slot_mapping, int32_t num_heads, int32_t row_bytes, int32_t block_size,
     int64_t num_slots) {
   const int64_t t = blockIdx.x;
-  const int64_t slot = slot_mapping[t];
+  const int64_t slot = load_uniform(slot_mapping, t);
   if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot / block_size;
-  const int64_t off = slot % block_size;
   const int chunks_per_row = row_bytes >> 4;
   const int per_tensor = num_heads * chunks_per_row;
-  for (int idx = threadIdx.x; idx < 2 * per_tensor; idx += kCacheThreads) {
-    const bool is_v = idx >= per_tensor;
-    const int r = is_v ? idx - per_tensor : idx;
-    const int h = r / chunks_per_row;
-    const int c = r - h * chunks_per_row;
-    const char *src = (is_v ? value + t * value_stride_bytes : key + t * key_stride_bytes) +
-                      (int64_t)h * row_bytes + c * 16;
-    char *dst = (is_v ? v_cache : k_cache) + ((blk * num_heads + h) * block_size + off) * row_bytes + c * 16;
-    *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
-  }
+  const int idx = blockIdx.y * kCacheThreads + threadIdx.x;
+  if (idx >= 2 * per_tensor) return;
+  const int64_t blk = slot / block_size;
+  const int64_t off = slot % block_size;
+  const bool is_v = idx >= per_tensor;
+  const int r = is_v ? idx - per_tensor : idx;
+  const int h = r / chunks_per_row;
+  const int c = r - h * chunks_per_row;
+  const char *src = (is_v ? value + t * value_stride_bytes : key + t * key_stride_bytes) + (int64_t)h * row_bytes +
+                    c * 16;
+  char *dst = (is_v ? v_cache : k_cache) + ((blk * num_heads + h) * block_size + off) * row_bytes + c * 16;
+  *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
 }
 
 hipError_t launch_reshape_and_cache(const void *key, const void *value, int64_t key_stride_bytes,
@@ -51,12 +55,17 @@ hipError_t launch_reshape_and_cache(const void *key, const void *value, int64_t 
                                     const int64_t *slot_mapping, int64_t num_tokens, int32_t num_heads,
                                     int32_t row_bytes, int32_t block_size, int64_t num_blocks,
                                     hipStream_t stream) {
+  // Chunks of one token's K and V rows, in workgroups of kCacheThreads lanes
+  // (the host bounds 2 * num_heads * row_bytes / 16 below 2^31).
+  const int64_t chunks = 2 * (int64_t)num_heads * (row_bytes / 16);
+  const int64_t parts = (chunks + kCacheThreads - 1) / kCacheThreads;
+  if (parts > 65535) return hipErrorInvalidValue;
   // grid.x is at most 2^31-1; split very long mappings into several launches.
   const int64_t kMaxGrid = 0x7fffffff;
   for (int64_t first = 0; first < num_tokens; first += kMaxGrid) {
     const int64_t count = num_tokens - first < kMaxGrid ? num_tokens - first : kMaxGrid;
-    hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)count), dim3(kCacheThreads), 0, stream,
-                       reinterpret_cast<const char *>(key) + first * key_stride_bytes,
+    hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)count, (unsigned)parts), dim3(kCacheThreads), 0,
+                       stream, reinterpret_cast<const char *>(key) + first * key_stride_bytes,
                        reinterpret_cast<const char *>(value) + first * value_stride_bytes, key_stride_bytes,
                        value_stride_bytes, reinterpret_cast<char *>(k_cache), reinterpret_cast<char *>(v_cache),
                        slot_mapping + first, num_heads, row_bytes, block_size, num_blocks * block_size);

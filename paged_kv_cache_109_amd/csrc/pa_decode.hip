@@ -60,26 +60,11 @@ constexpr int kSelfPlanSeqs = 1024;
 
 __device__ __forceinline__ uint4 load16(const char *p) {
 #if PA_DECODE_NT
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
+  return load_nt16(p);
 #else
   return *reinterpret_cast<const uint4 *>(p);
 #endif
 }
-
-template <Dt T, int D>
-struct RowShape {
-  static constexpr int kEB = EltBytes<T>::value;
-  static constexpr int kRowBytes = D * kEB;          // one token row of one head
-  static constexpr int kLPT = kRowBytes / 16;        // lanes per token row
-  static constexpr int kGroups = kWave / kLPT;       // tokens per wave load
-  static constexpr int kNI = kDecodeTile / kGroups;  // loads per tile
-  static constexpr int kFE = Frag<T>::kElems;        // elements per lane fragment
-  static_assert(kRowBytes % 16 == 0 && kLPT >= 1 && kLPT <= kWave, "row must be whole fragments");
-  static_assert(kDecodeTile % kGroups == 0, "tile must be whole wave loads");
-  static_assert(kLPT * kFE == D, "fragments must tile the head");
-};
 
 __device__ __forceinline__ int clip_ctx(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
 __device__ __forceinline__ int tiles_of(int n) { return (n + kDecodeTile - 1) / kDecodeTile; }
@@ -386,14 +371,13 @@ __device__ __forceinline__ void merge_fragments(const DecodeArgs &a, uint32_t wa
   }
 }
 
-// kAppend: each sequence's newest token (position n - 1) comes from
-// a.new_key / a.new_value instead of the cache, and the wave that consumes
-// the tile holding it writes those rows into the cache.  Exactly one wave
-// consumes that tile of a (sequence, head) and it reads the token from the
-// new rows, so no wave of the launch reads the cache row being written.
+// kAppend: each sequence's newest token (position n - 1) is read from
+// a.new_key / a.new_value instead of the cache.  The pass only reads; the
+// rows are stored into the cache by the reduce pass, after every read of
+// this launch.
 template <Dt T, int D, int B, bool kAppend>
 __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_kernel(DecodeArgs a) {
-  using R = RowShape<T, D>;
+  using R = RowShape<T, D, kDecodeTile>;
   const int lane = threadIdx.x % kWave;
   const uint32_t w = blockIdx.x * kDecodeWavesPerGroup + wave_id_uniform();
   uint32_t G, total;
@@ -540,32 +524,6 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_
   // Fold one tile into the running state of the pair under the consume cursor.
   constexpr uint32_t kAll = (1u << R::kNI) - 1u;
   auto consume = [&](const uint4 *kf, uint4 *vf, const uint4 &qslot, uint32_t okm) {
-    // Append: the last tile of a pair holds position n - 1, whose rows were
-    // just loaded from the new rows; write them into its cache slot.  A
-    // token outside the pool is neither read nor written.
-    if constexpr (kAppend) {
-      if (cc.t + 1 == cc.nt) {
-        const int p = cc.n - 1;
-        const int r = p - (cc.st + cc.t * kDecodeTile);  // its row within the tile
-        const int32_t phys = entry(cc.s, p / B);
-        // The load holding row r, picked with masks: a select of the slot's
-        // registers would become one load at a computed index, which puts
-        // the whole ring in scratch memory.
-        uint4 kn = make_uint4(0, 0, 0, 0), vn = kn;
-#pragma unroll
-        for (int i = 0; i < R::kNI; ++i) {
-          const uint32_t m = i == r / R::kGroups ? ~0u : 0u;
-          kn.x |= kf[i].x & m, kn.y |= kf[i].y & m, kn.z |= kf[i].z & m, kn.w |= kf[i].w & m;
-          vn.x |= vf[i].x & m, vn.y |= vf[i].y & m, vn.z |= vf[i].z & m, vn.w |= vf[i].w & m;
-        }
-        if (phys >= 0 && grp == r % R::kGroups) {
-          const int64_t off =
-              (int64_t)phys * block_stride + ((int64_t)cc.h * B + p % B) * R::kRowBytes + col * 16;
-          *reinterpret_cast<uint4 *>(const_cast<char *>(kbase) + off) = kn;
-          *reinterpret_cast<uint4 *>(const_cast<char *>(vbase) + off) = vn;
-        }
-      }
-    }
     if (cc.t == 0 || cc.g == g0) {
       qcur = qslot;
       m_run = -INFINITY;
@@ -637,8 +595,40 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_
 // Merge the fragments of every pair cut by range boundaries.  Worker wave w
 // handles the pair holding its first tile when that pair started before its
 // range and ends inside it (so every fragment of the pair exists).
+//
+// Append (a.new_key set): first, every lane of the grid stores 16-byte
+// chunks of the newest tokens' K and V rows (position n - 1 of each
+// sequence, read by the partition pass from the new rows) into their cache
+// slots.  The partition pass has ended, so no read of the caches races with
+// these stores.  A sequence with n = 0, or whose table entry for position
+// n - 1 lies outside the pool, stores nothing.
 template <Dt T, int D>
 __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_reduce_kernel(DecodeArgs a) {
+  if (a.new_key) {
+    using R = RowShape<T, D, kDecodeTile>;
+    const int64_t row_chunks = (int64_t)a.num_heads * R::kLPT;  // chunks of one token's K (or V) rows
+    const int64_t total = (int64_t)a.num_seqs * 2 * row_chunks;
+    const int64_t block_stride = (int64_t)a.num_heads * a.block_size * R::kRowBytes;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
+         c += (int64_t)gridDim.x * blockDim.x) {
+      const int s = (int)(c / (2 * row_chunks));
+      const int64_t r = c - (int64_t)s * 2 * row_chunks;
+      const bool is_v = r >= row_chunks;
+      const int64_t rc = is_v ? r - row_chunks : r;
+      const int h = (int)(rc / R::kLPT), col = (int)(rc % R::kLPT);
+      const int n = clip_ctx(a.context_lens[s], a.ctx_cap);
+      if (n < 1) continue;
+      const int p = n - 1;
+      const int32_t e = a.block_tables[(int64_t)s * a.max_blocks + p / a.block_size];
+      if (e < 0 || (int64_t)e >= a.num_blocks) continue;
+      const char *src = reinterpret_cast<const char *>(is_v ? a.new_value : a.new_key) +
+                        (int64_t)s * (is_v ? a.new_value_stride : a.new_key_stride) + h * R::kRowBytes + col * 16;
+      char *dst = reinterpret_cast<char *>(const_cast<void *>(is_v ? a.v_cache : a.k_cache)) +
+                  (int64_t)e * block_stride + ((int64_t)h * a.block_size + p % a.block_size) * R::kRowBytes + col * 16;
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+    }
+    if (a.workers <= 1) return;  // no pair was cut
+  }
   // Every worker wave v that the loop below visits has a non-empty range
   // (the plan never uses more workers than tiles) and wrote its fragment.
   const uint32_t G = a.plan[1];
@@ -774,7 +764,7 @@ static hipError_t launch_red(const DecodeArgs &a, int D, hipStream_t st) {
 }
 
 hipError_t launch_decode_reduce(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream) {
-  if (a.num_seqs == 0 || a.workers <= 1) return hipSuccess;
+  if (a.num_seqs == 0 || (a.workers <= 1 && !a.new_key)) return hipSuccess;
   switch (static_cast<Dt>(dtype)) {
     case Dt::F32: return launch_red<Dt::F32>(a, head_dim, stream);
     case Dt::F16: return launch_red<Dt::F16>(a, head_dim, stream);

@@ -112,6 +112,31 @@ __device__ __forceinline__ uint4 frag_pack(const float *x) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// ------------------------------------------------- K/V rows on wave lanes
+// The K (or V) row of one token and head is D elements, D*elt contiguous
+// bytes in the cache.  The decode-style kernels cover a row with kLPT
+// lanes doing one 16-byte load each, so one wave load covers kGroups
+// consecutive tokens and a tile of kTile tokens takes kNI loads.
+template <Dt T, int D, int kTile>
+struct RowShape {
+  static constexpr int kEB = EltBytes<T>::value;
+  static constexpr int kRowBytes = D * kEB;         // one token row of one head
+  static constexpr int kLPT = kRowBytes / 16;       // lanes per token row
+  static constexpr int kGroups = kWave / kLPT;      // tokens per wave load
+  static constexpr int kNI = kTile / kGroups;       // loads per tile
+  static constexpr int kFE = Frag<T>::kElems;       // elements per lane fragment
+  static_assert(kRowBytes % 16 == 0 && kLPT >= 1 && kLPT <= kWave, "row must be whole fragments");
+  static_assert(kTile % kGroups == 0, "tile must be whole wave loads");
+  static_assert(kLPT * kFE == D, "fragments must tile the head");
+};
+
+// 16 bytes, non-temporal: K/V bytes that a launch reads exactly once.
+__device__ __forceinline__ uint4 load_nt16(const char *p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ------------------------------------------------------------ lane exchange
 // DPP controls (GCN/CDNA encoding): quad_perm [1,0,3,2] and [2,3,0,1],
 // row_half_mirror (lane i of an 8-lane half-row reads lane 7-i), row_mirror

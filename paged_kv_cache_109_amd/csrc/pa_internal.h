@@ -29,6 +29,7 @@ struct DecodeArgs {
   int32_t num_seqs;
   int32_t max_blocks;
   int32_t num_heads;
+  int32_t block_size;     // tokens per cache block
   int32_t ctx_cap;        // context lengths are clipped to [0, ctx_cap]
   int32_t workers;        // worker waves launched (the split of the tile stream)
   int32_t out_row_words;  // 32-bit words of one sequence's output rows (H*D*elt/4)
@@ -43,8 +44,9 @@ struct DecodeArgs {
   int32_t suffix_row;  // floats of suffix_out per sequence: num_heads * (head_dim + 2)
   // Fused append only (both null otherwise): the K and V rows ([H][D]) of
   // each sequence's newest token, position n - 1, new_*_stride bytes apart.
-  // The pass reads that position from them instead of the cache and writes
-  // them into the cache (k_cache / v_cache are then writable).
+  // The partition pass reads that position from them instead of the cache;
+  // the reduce pass writes them into the cache (k_cache / v_cache are then
+  // writable).
   const void *new_key;
   const void *new_value;
   int64_t new_key_stride;

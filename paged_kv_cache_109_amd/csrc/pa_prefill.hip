@@ -104,10 +104,12 @@ __device__ __forceinline__ uint4 load16(const char *p) { return *reinterpret_cas
 // dst + 16*i; dst must be wave-uniform; M0 holds the LDS address).  Issued
 // as inline assembly so the compiler does not track it: its own tracking of
 // these loads loses the ring slots apart at loop joins and drains every
-// load in flight before some operand reads.  Every read of the ring is
+// load in flight before some operand reads (the compiler builtin for this
+// load measured 5% slower for that reason).  Every read of the ring is
 // ordered after its load by this kernel's own s_waitcnt vmcnt and barrier.
-// The compiler reserves M0 and ignores the clobber; nothing else in this
-// kernel uses M0.
+// M0 is a register the compiler reserves: it does not honour the clobber
+// (it warns so) and keeps no value of its own in M0 across these
+// statements -- this kernel's code has no other use of M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void load_lds16(const char *src, const lds_char *dst) {
@@ -498,6 +500,11 @@ prefill_chunk_kernel(PrefillArgs a, int qtiles) {
         }
       }
     };
+    // The ring's loads are ordered before these reads by the waits above;
+    // wait for them explicitly too, so that this copy does not depend on
+    // how the pipeline ends.
+    __builtin_amdgcn_s_waitcnt(WaitVm<0>::value);
+    asm volatile("" ::: "memory");
     store_slot(S0{});
     store_slot(S1{});
     store_slot(S2{});

@@ -28,19 +28,9 @@ namespace {
 constexpr int kGenQueries = 8;  // queries per wave
 constexpr int kGenDepth = 2;    // tiles in flight per wave
 
-template <Dt T, int D>
-struct GenRow {
-  static constexpr int kEB = EltBytes<T>::value;
-  static constexpr int kRowBytes = D * kEB;
-  static constexpr int kLPT = kRowBytes / 16;
-  static constexpr int kGroups = kWave / kLPT;
-  static constexpr int kNI = kDecodeTile / kGroups;
-  static constexpr int kFE = Frag<T>::kElems;
-};
-
 template <Dt T, int D, int B>
 __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void prefill_general_kernel(PrefillArgs a, int qgroups) {
-  using R = GenRow<T, D>;
+  using R = RowShape<T, D, kDecodeTile>;
   constexpr int kQ = kGenQueries;
   const int lane = threadIdx.x % kWave;
   const int w = blockIdx.x * kDecodeWavesPerGroup + wave_id_uniform();

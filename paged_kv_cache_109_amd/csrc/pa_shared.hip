@@ -34,22 +34,6 @@ namespace pa {
 
 namespace {
 
-template <Dt T, int D>
-struct Row {
-  static constexpr int kEB = EltBytes<T>::value;
-  static constexpr int kRowBytes = D * kEB;
-  static constexpr int kLPT = kRowBytes / 16;
-  static constexpr int kGroups = kWave / kLPT;
-  static constexpr int kNI = kDecodeTile / kGroups;
-  static constexpr int kFE = Frag<T>::kElems;
-};
-
-__device__ __forceinline__ uint4 load_nt(const char *p) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 __device__ __forceinline__ int clamp_len(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
 
 }  // namespace
@@ -58,7 +42,7 @@ constexpr int kPrefixDepth = 2;  // tiles in flight per wave
 
 template <Dt T, int D, int B>
 __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_prefix_kernel(SharedArgs a) {
-  using R = Row<T, D>;
+  using R = RowShape<T, D, kDecodeTile>;
   constexpr int kM = kSharedMaxMembers;
   static_assert(B % kDecodeTile == 0, "a prefix tile must lie in one block");
   const int lane = threadIdx.x % kWave;
@@ -130,8 +114,8 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_prefix_ker
       const int pos = t * kDecodeTile + i * R::kGroups + grp;
       const int64_t off = phys >= 0 ? (int64_t)phys * block_stride + head_off + (int64_t)(pos % B) * R::kRowBytes
                                     : (int64_t)col * 16;
-      kb[d][i] = load_nt(kbase + off);
-      vb[d][i] = load_nt(vbase + off);
+      kb[d][i] = load_nt16(kbase + off);
+      vb[d][i] = load_nt16(vbase + off);
     }
   };
   auto consume = [&](int d) {

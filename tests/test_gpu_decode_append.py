@@ -61,10 +61,14 @@ def run_both(c, key, value, split_workers=0, key_dev=None, value_dev=None, poiso
     out_f = torch.empty_like(q)
     if split_call:
         ws = pa.alloc_decode_workspace(S, H, D, max_ctx, B, split_workers)
+        k0, v0 = k_f.clone(), v_f.clone()
         pa.paged_attention_decode_append_partitions(out_f, q, kd, vd, k_f, v_f, bt, ctx, max_ctx, c.scale,
                                                     workspace=ws, split_workers=split_workers)
-        pa.paged_attention_decode_reduce(out_f, ctx, max_ctx, c.max_blocks_per_seq, H, D, B, workspace=ws,
-                                         split_workers=split_workers)
+        torch.cuda.synchronize()
+        # The partition pass only reads: the caches are untouched until the reduce.
+        assert same_bytes(k_f, k0) and same_bytes(v_f, v0)
+        pa.paged_attention_decode_append_reduce(out_f, q, kd, vd, k_f, v_f, bt, ctx, max_ctx, c.scale,
+                                                workspace=ws, split_workers=split_workers)
     else:
         pa.paged_attention_decode_append(out_f, q, kd, vd, k_f, v_f, bt, ctx, max_ctx, c.scale,
                                          split_workers=split_workers)
@@ -106,10 +110,11 @@ def test_append_any_split(split_workers):
     check_case(c, key, value, f"split {split_workers}", split_workers=split_workers)
 
 
-def test_append_partitions_then_reduce():
+@pytest.mark.parametrize("split_workers", [1, 200, 0])
+def test_append_partitions_then_reduce(split_workers):
     c = W.make_decode_case(5, 8, 128, 16, "bf16", [100, 2048, 31, 512, 7], seed=8, max_blocks_per_seq=128)
     key, value = new_rows(np.random.default_rng(2), 5, 8, 128, "bf16")
-    check_case(c, key, value, "two calls", split_call=True, split_workers=200)
+    check_case(c, key, value, "two calls", split_call=True, split_workers=split_workers)
 
 
 def test_append_never_reads_the_stale_slot():
