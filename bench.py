@@ -449,6 +449,9 @@ def run_decode(name, args, stream_read, cpu_seconds):
         print(f"[bench] swap_blocks {P} blocks x 2 caches: to host {swap_bytes / sw['out'] / 1e9:.1f} GB/s, "
               f"from host {swap_bytes / sw['in'] / 1e9:.1f} GB/s", file=sys.stderr, flush=True)
         del host_pool
+    if copies and B < 16:
+        components["decode_shared"] = {"skipped": "the shared-prefix decode is built for block sizes 16, 32, 64"}
+    if copies and B >= 16:
         # The same step with the sharing-aware decode: each group's shared
         # prompt blocks are read once for all of its samples.
         first = case.block_tables[:, 0]
@@ -515,7 +518,8 @@ def run_decode(name, args, stream_read, cpu_seconds):
                    "split_workers": workers or pa.decode_default_workers(tdt, D, B), "pool_replicas": args.replicas,
                    "step_launch": launch,
                    "step": ("copy_blocks(CoW pairs) + " if copies else "")
-                   + ("decode partitions with the new tokens' cache write fused in + decode reduce" if fused else
+                   + ("decode partitions (new tokens read from their rows) + decode reduce (stores them into the cache)"
+                      if fused else
                       ("reshape_and_cache(new tokens) + " if writes else "") + "decode partitions + decode reduce")},
         "per_model_step": {"layers": MODEL_LAYERS, "tokens_per_s": tokens_per_s / MODEL_LAYERS,
                            "ms_per_model_step": ms_per_step * MODEL_LAYERS,
