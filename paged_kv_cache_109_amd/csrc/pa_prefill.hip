@@ -25,8 +25,15 @@
 //
 // Per block a wave computes S^T = K Q^T with 8 v_mfma_f32_16x16x32 (two
 // 16-key tiles x four 32-wide steps of the head dimension; bf16 or f16 in,
-// fp32 out) and O^T += V^T P^T with 8 more (16 for bf16, whose P is carried
-// as a high and a low bf16 term to keep the weights' precision).  Working
+// fp32 out) and O^T += V^T P^T with 8 more, always in f16: bf16 keeps too
+// few bits for the weights P, so for bf16 caches each wave rewrites the V
+// rows it loaded into the ring as f16 once (exact inside f16's range; below
+// 2^-14 the error is under 2^-25 absolute) and P goes in as f16.  A V value
+// beyond f16's range turns into inf there, which leaves the accumulators of
+// every wave that reads it non-finite; such a wave (as any wave whose
+// accumulators end non-finite, e.g. 0 * NaN from a key it must not see)
+// recomputes its queries key by key in fp32 straight from the cache, so
+// the result is exact for any input and the fast path pays nothing.  Working
 // transposed keeps one query per lane column: lane (g, n) holds query n's
 // scores of keys 16*mt + 4g + j (tile mt, register j), and those eight
 // registers, packed, are exactly its B operand of the P V product -- the
@@ -86,6 +93,8 @@ template <int N>
 struct WaitVm : std::integral_constant<int, 0x0F70 | (N & 15) | ((N >> 4) << 14)> {
   static_assert(N >= 0 && N < 64, "vmcnt range");
 };
+// s_waitcnt immediate that waits for this wave's LDS (and scalar) operations.
+struct WaitLgkm0 : std::integral_constant<int, 0xC07F> {};
 
 template <Dt T>
 __device__ __forceinline__ f32x4 mfma(const uint4 &a, const uint4 &b, const f32x4 &c) {
@@ -99,6 +108,22 @@ __device__ __forceinline__ f32x4 mfma(const uint4 &a, const uint4 &b, const f32x
 }
 
 __device__ __forceinline__ uint4 load16(const char *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// Eight 16-bit values of dtype T (one 16-byte chunk) as floats.
+template <Dt T>
+__device__ __forceinline__ void widen8(const uint4 &w, float (&f)[8]) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (T == Dt::BF16) {
+      f[2 * i] = __uint_as_float(u[i] << 16);
+      f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    } else {
+      f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[i] & 0xffffu));
+      f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[i] >> 16));
+    }
+  }
+}
 
 // 16 bytes per lane from global memory straight into LDS (lane i writes
 // dst + 16*i; dst must be wave-uniform; M0 holds the LDS address).  Issued
@@ -247,6 +272,11 @@ prefill_chunk_kernel(PrefillArgs a, int qtiles) {
   // Append: a chunk key (position >= c) is row q0 + key - c of the new rows;
   // its offsets from the cache bases, valid while that row lies in q (the
   // row index comes from device data).
+  // Append: this tile's own tokens are keys tok_lo .. tok_hi-1; those at or
+  // past ring_lo are still in the ring when the loop ends.
+  [[maybe_unused]] const int tok_lo = max(c + qbase, 0), tok_hi = min(c + qbase + kPfQ, n);
+  [[maybe_unused]] const int ring_lo = max(nkb - kPfRing, 0) * kPfKeys;
+  [[maybe_unused]] const int store_lo = max(tok_lo, ring_lo);
   [[maybe_unused]] const int64_t knew = kAppend ? (int64_t)((uintptr_t)a.new_key - (uintptr_t)kbase) +
                                                       (int64_t)h * (kPfD * 2) + chunk_off : 0;
   [[maybe_unused]] const int64_t vnew = kAppend ? (int64_t)((uintptr_t)a.new_value - (uintptr_t)vbase) +
@@ -287,6 +317,8 @@ prefill_chunk_kernel(PrefillArgs a, int qtiles) {
   const int wave_first = c + qbase + wave * kPfWaveQ;
   const bool wave_full = __builtin_amdgcn_ballot_w64(q_ok) == ~0ull;
   const float sc = a.scale_log2;  // > 0 (checked by the host)
+  // log2 of the factor on the bf16 kernel's weights (see the weights below).
+  constexpr float kPScale = T == Dt::BF16 ? 7.f : 0.f;
 
   // Per-lane LDS offsets of the MFMA operands (tile or half t adds 16 rows).
   //  K (A of S^T, tile mt, step st): row 16*mt + col, chunk 4*st + g.
@@ -353,13 +385,11 @@ prefill_chunk_kernel(PrefillArgs a, int qtiles) {
 #pragma unroll
       for (int dt = 0; dt < kPfD / 16; ++dt) o[dt] *= alpha;
     }
-    const float m = (m_run == -INFINITY) ? 0.f : m_run;
-    // Weights p = 2^(x*scale_log2 - m) and P^T packed as the B operand
-    // (element e = 4*mt + j).  bf16 keeps only 8 significant bits, too few
-    // for the weights, so P is carried as P_hi + P_lo (P_hi the top 16 bits
-    // of the float, P_lo the rest rounded to bf16: about 16 bits together)
-    // and the product is formed twice; fp16's 11 bits are enough on their
-    // own.
+    // Weights p = 2^(x*scale_log2 - m) and P^T packed as the f16 B operand
+    // (element e = 4*mt + j).  For bf16 caches the weights are scaled by
+    // 2^7 (at most 2^15 under the lazy max, inside f16's range), which
+    // keeps small weights out of f16's subnormals; the scale cancels in O/l.
+    const float m = (m_run == -INFINITY) ? 0.f : m_run - kPScale;
     float p[8];
     float lsum = 0.f;
 #pragma unroll
@@ -368,27 +398,12 @@ prefill_chunk_kernel(PrefillArgs a, int qtiles) {
       lsum += p[e];
     }
     l_run += lsum;
-    uint32_t hw[4], lw[4];
+    uint32_t hw[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float p0 = p[2 * q], p1 = p[2 * q + 1];
-      if constexpr (T == Dt::BF16) {
-        const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
-        hw[q] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // high halves: p1 | p0
-        lw[q] = pack_pair<true>(p0 - __uint_as_float(b0 & 0xffff0000u), p1 - __uint_as_float(b1 & 0xffff0000u));
-      } else {
-        hw[q] = pack_pair<false>(p0, p1);
-        lw[q] = 0;
-      }
-    }
+    for (int q = 0; q < 4; ++q) hw[q] = pack_pair<false>(p[2 * q], p[2 * q + 1]);
     const uint4 pb = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    const uint4 pl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
 #pragma unroll
-    for (int dt = 0; dt < kPfD / 16; ++dt) {
-      const uint4 va = vread(ks, dt);
-      o[dt] = mfma<T>(va, pb, o[dt]);
-      if constexpr (T == Dt::BF16) o[dt] = mfma<T>(va, pl, o[dt]);
-    }
+    for (int dt = 0; dt < kPfD / 16; ++dt) o[dt] = mfma<Dt::F16>(vread(ks, dt), pb, o[dt]);
   };
 
   // Wait until at most N of this wave's loads are in flight, then meet the
@@ -405,18 +420,61 @@ prefill_chunk_kernel(PrefillArgs a, int qtiles) {
   // Loads per wave per block (K and V).
   constexpr int kL = 2 * kLoads;
   static_assert(kPfRing == 4, "the pipeline below is written for 4 slots");
+  // bf16: the V rows this wave loaded for block kb (slot sc_) rewritten as
+  // f16, in place.  The append kernel first stores the rows of this tile's
+  // own tokens into their cache slots as loaded (bf16), for the keys still
+  // in the ring at the end (the K rows follow from the ring after the loop).
+  auto convert = [&](int kb, auto sc_) __attribute__((always_inline)) {
+    if constexpr (T == Dt::BF16) {
+      char *p = vslot(sc_) + 1024 * wave + 16 * lane;
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        uint4 w = *reinterpret_cast<const uint4 *>(p + 1024 * kPfWaves * i);
+        if constexpr (kAppend) {
+          const int key = kb * kPfKeys + r0 + 4 * kPfWaves * i;
+          if (key >= store_lo && key < tok_hi && q0 >= 0 && q0 + key - c < a.total_q) {
+            const int32_t e = a.block_tables[table_row + (kb * kPfKeys + 4 * wave + 4 * kPfWaves * i) / B];
+            if (e >= 0 && (int64_t)e < a.num_blocks)
+              *reinterpret_cast<uint4 *>(const_cast<char *>(vbase) + (int64_t)e * block_stride +
+                                         (int64_t)(key & (B - 1)) * kRow + chunk_off) = w;
+          }
+        }
+        float f[8];
+        widen8<Dt::BF16>(w, f);
+        w = make_uint4(pack_pair<false>(f[0], f[1]), pack_pair<false>(f[2], f[3]), pack_pair<false>(f[4], f[5]),
+                       pack_pair<false>(f[6], f[7]));
+        *reinterpret_cast<uint4 *>(p + 1024 * kPfWaves * i) = w;
+      }
+    }
+  };
   // End of step kb: block kb+1 must be in; the blocks issued after it (up
-  // to two, fewer near the end) may stay in flight.
+  // to two, fewer near the end) may stay in flight.  For bf16 each wave
+  // already waited for its own loads of block kb+1 to convert them, so the
+  // barrier only has to follow its LDS writes.
   auto end_step = [&](int kb) __attribute__((always_inline)) {
-    const int after = min(nkb - 1, kb + 3) - (kb + 1);
-    if (after >= 2) sync_blocks(WaitVm<2 * kL>{});
-    else if (after == 1) sync_blocks(WaitVm<kL>{});
-    else sync_blocks(WaitVm<0>{});
+    if constexpr (T == Dt::BF16) {
+      sync_blocks(WaitLgkm0{});
+    } else {
+      const int after = min(nkb - 1, kb + 3) - (kb + 1);
+      if (after >= 2) sync_blocks(WaitVm<2 * kL>{});
+      else if (after == 1) sync_blocks(WaitVm<kL>{});
+      else sync_blocks(WaitVm<0>{});
+    }
   };
   // Step kb: block kb is in slot kb % 4; the load of block kb+3 goes into
   // the slot block kb-1 used, with the table entries fetched a step before.
+  // bf16 first converts this wave's part of block kb+1 (slot ns), waiting
+  // for its loads with block kb+2's still in flight.
   uint32_t ent[kLoads];  // table entries of the next block to load
-  auto step = [&](int kb, auto ks, auto ds) __attribute__((always_inline)) {
+  auto step = [&](int kb, auto ks, auto ds, auto ns) __attribute__((always_inline)) {
+    if constexpr (T == Dt::BF16) {
+      if (kb + 1 < nkb) {
+        if (kb + 2 < nkb) __builtin_amdgcn_s_waitcnt(WaitVm<kL>::value);
+        else __builtin_amdgcn_s_waitcnt(WaitVm<0>::value);
+        asm volatile("" ::: "memory");
+        convert(kb + 1, ns);
+      }
+    }
     if (kb + 3 < nkb) {
       load_block(kb + 3, ent, ds);
       if (kb + 4 < nkb) entries(kb + 4, ent);
@@ -444,46 +502,132 @@ prefill_chunk_kernel(PrefillArgs a, int qtiles) {
       load_block(2, ent, S2{});
     }
     if (nkb > 3) entries(3, ent);
-    // Block 0 in; blocks 1 and 2 may stay in flight.
-    if (nkb > 2) sync_blocks(WaitVm<2 * kL>{});
-    else if (nkb == 2) sync_blocks(WaitVm<kL>{});
-    else sync_blocks(WaitVm<0>{});
+    // Block 0 in (converted, for bf16); blocks 1 and 2 may stay in flight.
+    if constexpr (T == Dt::BF16) {
+      if (nkb > 2) __builtin_amdgcn_s_waitcnt(WaitVm<2 * kL>::value);
+      else if (nkb == 2) __builtin_amdgcn_s_waitcnt(WaitVm<kL>::value);
+      else __builtin_amdgcn_s_waitcnt(WaitVm<0>::value);
+      asm volatile("" ::: "memory");
+      convert(0, S0{});
+      sync_blocks(WaitLgkm0{});
+    } else {
+      if (nkb > 2) sync_blocks(WaitVm<2 * kL>{});
+      else if (nkb == 2) sync_blocks(WaitVm<kL>{});
+      else sync_blocks(WaitVm<0>{});
+    }
     for (int kb = 0;; kb += 4) {
-      step(kb, S0{}, S3{});
+      step(kb, S0{}, S3{}, S1{});
       if (kb + 1 >= nkb) break;
-      step(kb + 1, S1{}, S0{});
+      step(kb + 1, S1{}, S0{}, S2{});
       if (kb + 2 >= nkb) break;
-      step(kb + 2, S2{}, S1{});
+      step(kb + 2, S2{}, S1{}, S3{});
       if (kb + 3 >= nkb) break;
-      step(kb + 3, S3{}, S2{});
+      step(kb + 3, S3{}, S2{}, S0{});
       if (kb + 4 >= nkb) break;
     }
   }
 
-  // ---- write this lane's query: dimensions 16*dt + 4*g .. +3.
-  float l = l_run + __shfl_xor(l_run, 16, kWave);
-  l += __shfl_xor(l, 32, kWave);
-  if (q_ok) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    char *orow = reinterpret_cast<char *>(a.out) + ((int64_t)(q0 + jq) * a.num_heads + h) * (kPfD * 2);
+  char *orow = reinterpret_cast<char *>(a.out) + ((int64_t)(q_ok ? q0 + jq : 0) * a.num_heads + h) * (kPfD * 2);
+  bool bad = false;
 #pragma unroll
-    for (int dt = 0; dt < kPfD / 16; ++dt) {
-      const uint2 w = make_uint2(pack_pair<T == Dt::BF16>(o[dt][0] * inv, o[dt][1] * inv),
-                                 pack_pair<T == Dt::BF16>(o[dt][2] * inv, o[dt][3] * inv));
-      *reinterpret_cast<uint2 *>(orow + (16 * dt + 4 * g) * 2) = w;
+  for (int dt = 0; dt < kPfD / 16; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bad |= !__builtin_isfinite(o[dt][j]);
+  if (__builtin_amdgcn_ballot_w64(bad) == 0) {
+    // ---- write this lane's query: dimensions 16*dt + 4*g .. +3.
+    float l = l_run + __shfl_xor(l_run, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    if (q_ok) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < kPfD / 16; ++dt) {
+        const uint2 w = make_uint2(pack_pair<T == Dt::BF16>(o[dt][0] * inv, o[dt][1] * inv),
+                                   pack_pair<T == Dt::BF16>(o[dt][2] * inv, o[dt][3] * inv));
+        *reinterpret_cast<uint2 *>(orow + (16 * dt + 4 * g) * 2) = w;
+      }
+    }
+  } else {
+    // ---- exact recomputation of the wave's queries, key by key in fp32
+    // with an online softmax, K/V read straight from the cache (the chunk's
+    // keys from the new rows in the append kernel).  Lane (g, n) keeps
+    // dimensions 32*st + 8*g .. +7 of query n, the layout of its Q
+    // fragments; the four lane groups add their parts of each score.
+    float qv[kPfD / 4], acc[kPfD / 4];
+#pragma unroll
+    for (int st = 0; st < kPfD / 32; ++st) {
+      float f[8];
+      widen8<T>(qf[st], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        qv[8 * st + i] = f[i];
+        acc[8 * st + i] = 0.f;
+      }
+    }
+    float me = -INFINITY, le = 0.f;
+    const int last = q_ok ? qpos : -1;
+    const int wave_end = min(wave_last, n - 1);
+    for (int key = 0; key <= wave_end; ++key) {
+      const char *krow, *vrow;
+      const int row = q0 + key - c;
+      if (kAppend && key >= c && q0 >= 0 && row < a.total_q) {
+        krow = reinterpret_cast<const char *>(a.new_key) + (int64_t)row * a.new_key_stride + (int64_t)h * kRow;
+        vrow = reinterpret_cast<const char *>(a.new_value) + (int64_t)row * a.new_value_stride + (int64_t)h * kRow;
+      } else {
+        const int32_t v = load_uniform(a.block_tables, table_row + key / B);
+        const uint32_t e = (v >= 0 && (int64_t)v < a.num_blocks) ? (uint32_t)v : 0u;
+        const uint64_t off = (uint64_t)e * block_stride + (uint32_t)(key & (B - 1)) * kRow;
+        krow = kbase + off;
+        vrow = vbase + off;
+      }
+      float d = 0.f;
+#pragma unroll
+      for (int st = 0; st < kPfD / 32; ++st) {
+        float f[8];
+        widen8<T>(load16(krow + 16 * (4 * st + g)), f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d = fmaf(qv[8 * st + i], f[i], d);
+      }
+      d += __shfl_xor(d, 16, kWave);
+      d += __shfl_xor(d, 32, kWave);
+      if (key <= last) {
+        const float s = d * sc;
+        const float mn = fmaxf(me, s);
+        const float al = fast_exp2(me - mn);
+        const float pw = fast_exp2(s - mn);
+        le = le * al + pw;
+#pragma unroll
+        for (int st = 0; st < kPfD / 32; ++st) {
+          float f[8];
+          widen8<T>(load16(vrow + 16 * (4 * st + g)), f);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[8 * st + i] = fmaf(acc[8 * st + i], al, pw * f[i]);
+        }
+        me = mn;
+      }
+    }
+    if (q_ok) {
+      const float inv = le > 0.f ? 1.f / le : 0.f;
+#pragma unroll
+      for (int st = 0; st < kPfD / 32; ++st) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w[i] = pack_pair<T == Dt::BF16>(acc[8 * st + 2 * i] * inv, acc[8 * st + 2 * i + 1] * inv);
+        *reinterpret_cast<uint4 *>(orow + 16 * (4 * st + g)) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
     }
   }
 
   // ---- append: write the K/V rows of this tile's tokens (chunk indices
   // qbase .. qbase+kPfQ-1, keys tok_lo .. tok_hi-1) into their cache slots.
   // The ring still holds the last four blocks, loaded from the new rows:
-  // each lane stores the 16 bytes it loaded there for every such key.  Keys
-  // in an older block (at most kPfKeys-1 of them, when the tile does not
-  // start on a block) are copied from the new rows.  Tokens outside the
-  // context or q, or whose table entry lies outside the pool, are skipped.
+  // each lane stores the 16 bytes it loaded there for every such key (for
+  // bf16 only the K rows: its V rows were stored before they were
+  // converted).  Keys in an older block (at most kPfKeys-1 of them, when the
+  // tile does not start on a block) are copied from the new rows.  Tokens
+  // outside the context or q, or whose table entry lies outside the pool,
+  // are skipped.
   if constexpr (kAppend) {
-    const int tok_lo = max(c + qbase, 0), tok_hi = min(c + qbase + kPfQ, n);
-    const int ring_lo = max(nkb - kPfRing, 0) * kPfKeys;  // first key still in the ring
     auto store_slot = [&](auto sc) __attribute__((always_inline)) {
       constexpr int j = decltype(sc)::value;
       // The block in slot j: the last one below nkb that is j mod 4.
@@ -496,7 +640,8 @@ prefill_chunk_kernel(PrefillArgs a, int qtiles) {
           const int64_t d = (int64_t)e * block_stride + (int64_t)(key & (B - 1)) * kRow + chunk_off;
           const int l = 1024 * wave + 16 * lane;
           *reinterpret_cast<uint4 *>(const_cast<char *>(kbase) + d) = *reinterpret_cast<const uint4 *>(kslot(sc) + l);
-          *reinterpret_cast<uint4 *>(const_cast<char *>(vbase) + d) = *reinterpret_cast<const uint4 *>(vslot(sc) + l);
+          if constexpr (T != Dt::BF16)
+            *reinterpret_cast<uint4 *>(const_cast<char *>(vbase) + d) = *reinterpret_cast<const uint4 *>(vslot(sc) + l);
         }
       }
     };

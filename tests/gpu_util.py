@@ -63,6 +63,23 @@ def check_attention(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str = 
     return max_abs, max_rel
 
 
+def plant_value(case, seq: int, pos: int, head: int, dims, values=None) -> None:
+    """Write float32 `values` (NaN when None) at V dimensions `dims` of the
+    token at position `pos` of sequence `seq`, head `head`: into the pool for
+    a cached token, into new_value for a token of the chunk."""
+    import workloads as W
+    ql = int(case.cu_q_lens[seq + 1] - case.cu_q_lens[seq])
+    cached = int(case.context_lens[seq]) - ql
+    if pos < cached:
+        arr, idx = case.v_cache, (case.seq_blocks[seq][pos // case.block_size], head, pos % case.block_size, dims)
+    else:
+        arr, idx = case.new_value, (int(case.cu_q_lens[seq]) + pos - cached, head, dims)
+    if values is None:
+        W.poison(arr, case.dtype, idx)
+    else:
+        arr[idx] = W.cast(np.asarray(values, np.float32), case.dtype)
+
+
 def device_slots(case, block_tables=None) -> torch.Tensor:
     """Device int64 slot mapping of the case's new tokens, translated by the
     library (pa_slot_mapping) through its block tables."""

@@ -12,7 +12,7 @@ import torch
 import oracle
 import paged_kv_cache_109_amd as pa
 import workloads as W
-from gpu_util import DeviceCase, check_attention, dev, device_slots, host, say
+from gpu_util import DeviceCase, as_f64, check_attention, dev, device_slots, host, plant_value, say
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +74,36 @@ def test_prefill_poisoned_slots_are_never_read():
     out, ref = run_prefill(c, poison=True)
     assert torch.isfinite(out).all()
     check_attention(out, ref, "bf16", "poisoned")
+
+
+def test_prefill_bf16_values_beyond_f16_range():
+    """The P V product runs in f16, so bf16 V values past f16's range (a
+    cached token and a chunk token) leave the waves that read them with
+    non-finite sums; those waves recompute their queries exactly."""
+    c = W.make_prefill_case(3, 0, [40, 0, 200], 2, 128, 16, "bf16", seed=21, q_lens=[100, 64, 150], name="huge")
+    plant_value(c, 0, 10, 1, [0, 1, 2, 3], [1e5, -3e6, 1e30, 7e4])
+    plant_value(c, 2, 230, 0, [5], [2e5])
+    out, ref = run_prefill(c)
+    assert torch.isfinite(out).all()
+    say("  max err", check_attention(out, ref, "bf16", "V beyond f16's range"))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_nan_value_reaches_only_queries_that_see_it(dtype):
+    """A NaN in one V element of a chunk token: exactly the queries at or
+    past that position (that head, that dimension) come out NaN, as in the
+    oracle; the earlier queries of the same wave, whose weights for it are
+    0, stay exact."""
+    c = W.make_prefill_case(2, 0, [30, 5], 2, 128, 16, dtype, seed=22, q_lens=[90, 40], name="nan")
+    plant_value(c, 0, 70, 1, [7])
+    out, ref = run_prefill(c)
+    g, r = as_f64(out), ref
+    want = np.zeros(r.shape, bool)
+    want[int(c.cu_q_lens[0]) + 70 - 30: int(c.cu_q_lens[1]), 1, 7] = True
+    assert np.array_equal(np.isnan(r), want)
+    assert np.array_equal(np.isnan(g), want)
+    out[torch.from_numpy(want).to(out.device)] = 0
+    say("  max err", check_attention(out, np.where(want, 0.0, r), dtype, "NaN in one V element"))
 
 
 def test_single_query_chunk_equals_decode():

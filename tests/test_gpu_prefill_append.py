@@ -15,7 +15,7 @@ import torch
 import oracle
 import paged_kv_cache_109_amd as pa
 import workloads as W
-from gpu_util import check_attention, dev, host, say
+from gpu_util import check_attention, dev, host, plant_value, say
 
 pytestmark = pytest.mark.gpu
 
@@ -90,6 +90,16 @@ def test_prefill_append_chunked_prefill_full_size():
     out_f, k_f, v_f, out_s, k_s, v_s, _ = run_both(c)
     assert same_bytes(out_f, out_s) and same_bytes(k_f, k_s) and same_bytes(v_f, v_s)
     say("  chunked_prefill: fused = separate, bit for bit (output and both caches)")
+
+
+def test_prefill_append_bf16_values_beyond_f16_range():
+    # The waves that read them recompute their queries from the new rows
+    # (chunk tokens) and the cache (cached tokens).
+    c = W.make_prefill_case(3, 0, [40, 0, 200], 2, 128, 16, "bf16", seed=23, q_lens=[100, 64, 150], name="huge")
+    plant_value(c, 0, 10, 1, [0, 1, 2, 3], [1e5, -3e6, 1e30, 7e4])
+    plant_value(c, 0, 120, 0, [9], [-5e7])
+    plant_value(c, 2, 230, 1, [5], [2e5])
+    check_case(c, "V beyond f16's range")
 
 
 def test_prefill_append_out_of_pool_entry_is_not_written():

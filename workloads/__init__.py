@@ -65,7 +65,7 @@ def poison(arr: np.ndarray, dtype: str, index) -> None:
     if dtype == "f32":
         arr[index] = np.nan
     else:
-        arr[index] = NAN_BITS[dtype]
+        arr.view(np.uint16)[index] = NAN_BITS[dtype]
 
 
 _CHUNK = 1 << 22
