@@ -38,6 +38,7 @@
 // each lane group keeps its own online-softmax state and fp32 value
 // accumulator, merged with lane swaps when a pair ends.
 
+#include <algorithm>
 #include <mutex>
 
 #include "pa_device.h"
@@ -602,15 +603,25 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_
 // slots.  The partition pass has ended, so no read of the caches races with
 // these stores.  A sequence with n = 0, or whose table entry for position
 // n - 1 lies outside the pool, stores nothing.
+// Workgroups of the reduce pass that merge cut pairs (none when no pair was
+// cut); any further ones store the new tokens of an append step.
+__host__ __device__ inline uint32_t reduce_merge_groups(const DecodeArgs &a) {
+  return a.workers > 1 ? (uint32_t)((a.workers + kDecodeWavesPerGroup - 1) / kDecodeWavesPerGroup) : 0u;
+}
+
 template <Dt T, int D>
 __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_reduce_kernel(DecodeArgs a) {
-  if (a.new_key) {
+  // The first reduce_merge_groups(a) workgroups merge cut pairs; the rest
+  // (append only) store the new tokens, so that the two chains of
+  // dependent loads run side by side.
+  const uint32_t merge_groups = reduce_merge_groups(a);
+  if (blockIdx.x >= merge_groups) {
     using R = RowShape<T, D, kDecodeTile>;
     const int64_t row_chunks = (int64_t)a.num_heads * R::kLPT;  // chunks of one token's K (or V) rows
     const int64_t total = (int64_t)a.num_seqs * 2 * row_chunks;
     const int64_t block_stride = (int64_t)a.num_heads * a.block_size * R::kRowBytes;
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
-         c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t step = (int64_t)(gridDim.x - merge_groups) * blockDim.x;
+    for (int64_t c = (int64_t)(blockIdx.x - merge_groups) * blockDim.x + threadIdx.x; c < total; c += step) {
       const int s = (int)(c / (2 * row_chunks));
       const int64_t r = c - (int64_t)s * 2 * row_chunks;
       const bool is_v = r >= row_chunks;
@@ -627,7 +638,7 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_reduce_ker
                   (int64_t)e * block_stride + ((int64_t)h * a.block_size + p % a.block_size) * R::kRowBytes + col * 16;
       *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
     }
-    if (a.workers <= 1) return;  // no pair was cut
+    return;
   }
   // Every worker wave v that the loop below visits has a non-empty range
   // (the plan never uses more workers than tiles) and wrote its fragment.
@@ -748,9 +759,20 @@ hipError_t launch_decode_partitions(const DecodeArgs &a, int dtype, int head_dim
   return hipErrorInvalidValue;
 }
 
+// Store workgroups: one 16-byte chunk per thread, at most kReduceStoreGroups
+// of them (grid-stride beyond).
+constexpr int64_t kReduceStoreGroups = 4096;
+
 template <Dt T>
 static hipError_t launch_red(const DecodeArgs &a, int D, hipStream_t st) {
-  const dim3 grid((unsigned)((a.workers + kDecodeWavesPerGroup - 1) / kDecodeWavesPerGroup));
+  int64_t store_groups = 0;
+  if (a.new_key) {
+    const int64_t chunks = (int64_t)a.num_seqs * 2 * a.num_heads * (D * (int64_t)EltBytes<T>::value / 16);
+    const int64_t threads = kDecodeWavesPerGroup * kWave;
+    store_groups = std::min<int64_t>((chunks + threads - 1) / threads, kReduceStoreGroups);
+  }
+  const dim3 grid((unsigned)(reduce_merge_groups(a) + store_groups));
+  if (grid.x == 0) return hipSuccess;
   switch (D) {
     case 64:
       hipLaunchKernelGGL((decode_reduce_kernel<T, 64>), grid, dim3(kDecodeWavesPerGroup * kWave), 0, st, a);
