@@ -466,7 +466,11 @@ pa_status pa_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t n
  *
  * fp16 and bf16 at head_dim 128 run on the matrix cores (MFMA); fp32, and
  * head_dim 64, run on the vector ALU (8 queries per wave, each K/V tile read
- * once for them).
+ * once for them).  The matrix kernel forms the weighted sum of V in fp16
+ * (for a bf16 cache it converts the V rows to fp16 on chip); a group of 16
+ * queries whose sums come out non-finite (a V value beyond fp16's range, or
+ * an inf/NaN in a row it must not see) is recomputed in fp32, so the result
+ * is within the attention tolerance for any finite input.
  *
  *  out, q          device [total_q][num_heads][head_dim], `dtype`.
  *  cu_q_lens       device int32 [num_seqs + 1], non-decreasing, from 0 to
