@@ -12,7 +12,7 @@
 //
 // Mapping to CDNA4.  A workgroup of 8 waves takes 128 queries of one
 // (sequence, head); each wave owns 16 of them, one per column of a 16x16
-// MFMA tile.  A wave needs about 100 VGPRs, so two workgroups share a CU at
+// MFMA tile.  A wave needs at most 128 VGPRs, so two workgroups share a CU at
 // four waves per SIMD: while one wave waits on LDS, an exp chain or the
 // matrix core, another issues.  The q tiles of one (sequence, head) get
 // workgroup ids equal mod 8, so they run on one XCD and read its K/V
@@ -424,6 +424,8 @@ prefill_chunk_kernel(PrefillArgs a, int qtiles) {
   // f16, in place.  The append kernel first stores the rows of this tile's
   // own tokens into their cache slots as loaded (bf16), for the keys still
   // in the ring at the end (the K rows follow from the ring after the loop).
+  // Those stores count in vmcnt; the ring's loads complete in order, so a
+  // wait for a block's loads stays exact and at most also waits for them.
   auto convert = [&](int kb, auto sc_) __attribute__((always_inline)) {
     if constexpr (T == Dt::BF16) {
       char *p = vslot(sc_) + 1024 * wave + 16 * lane;
