@@ -117,6 +117,19 @@ def test_append_partitions_then_reduce(split_workers):
     check_case(c, key, value, "two calls", split_call=True, split_workers=split_workers)
 
 
+@pytest.mark.parametrize("split_workers", [0, 1])
+def test_append_more_rows_than_one_pass_of_the_store_grid(split_workers):
+    # 900 sequences x 40 heads of head_dim 128 (f16) make 1,152,000 16-byte
+    # chunks of new rows, more than the reduce's store workgroups cover in one
+    # pass (4096 x 256 threads), so its grid-stride loop runs; at one worker
+    # no pair is cut and every workgroup of the reduce stores.
+    S = 900
+    lens = np.random.default_rng(13).integers(1, 40, S).tolist()
+    c = W.make_decode_case(S, 40, 128, 16, "f16", lens, seed=13, max_blocks_per_seq=3)
+    key, value = new_rows(np.random.default_rng(14), S, 40, 128, "f16")
+    check_case(c, key, value, f"{S} sequences, split {split_workers}", split_workers=split_workers)
+
+
 def test_append_never_reads_the_stale_slot():
     c = W.make_decode_case(4, 4, 128, 16, "f16", [1, 16, 17, 250], seed=9, max_blocks_per_seq=16)
     key, value = new_rows(np.random.default_rng(3), 4, 4, 128, "f16")
