@@ -186,14 +186,18 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_prefix_ker
 
 // out[s][h] for member j of group g: the prefix chunks' partials and the
 // pass's partial of s's own positions, rescaled to a common max.  One wave
-// per (group, member, head); lanes stride over the head dimension.  The
-// work is a few small reads, so their latency is what counts: each step's
-// loads are issued together (all member ids, then the chunk headers as
-// scalar loads, then the partial rows) before any of them is used.
+// per (group, member, head); lane l holds dimensions l, l+64, ...  The work
+// is a few small reads, so their latency is what counts.  The partials of
+// the first kU chunks depend only on (g, j, h), so they are loaded before
+// the member ids, and the member's own row right after them: two round trips
+// to memory in the usual case of at most kU chunks.  The sums run over the
+// suffix and then the chunks in order, whichever loop a chunk's loads are in.
 template <Dt T, int D>
 __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_combine_kernel(SharedArgs a) {
   constexpr int kM = kSharedMaxMembers;
-  constexpr int kU = 4;  // chunks whose loads are in flight together
+  constexpr int kU = 4;                   // chunks loaded up front (and per later batch)
+  constexpr int kPer = D / kWave;         // dimensions per lane
+  static_assert(D % kWave == 0, "head_dim is whole waves");
   const int lane = threadIdx.x % kWave;
   const int w = blockIdx.x * kDecodeWavesPerGroup + wave_id_uniform();
   const int H = a.num_heads;
@@ -201,6 +205,18 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_combine_ke
   const int j = (w / H) % kM;
   const int g = w / (H * kM);
   if (g >= a.num_groups) return;
+  const int C = a.chunks;
+  const int64_t chunk_stride = (int64_t)H * kM * (D + 2);  // floats from chunk c to c+1
+  const float *part0 = a.partials + (((int64_t)g * C * H + h) * kM + j) * (D + 2);
+  float mc0[kU], lc0[kU], v0[kU][kPer];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const bool in = u < C;
+    mc0[u] = in ? load_uniform(part0 + u * chunk_stride, D) : -INFINITY;
+    lc0[u] = in ? load_uniform(part0 + u * chunk_stride, D + 1) : 0.f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v0[u][i] = in ? part0[u * chunk_stride + lane + kWave * i] : 0.f;
+  }
   // Member j exists only inside the leading run of valid ids (as the prefix
   // kernel counts them).
   int ids[kM];
@@ -210,18 +226,20 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_combine_ke
   for (int i = 0; i < kM; ++i)
     if (i <= j && (ids[i] < 0 || ids[i] >= a.num_seqs)) return;
   const int s = ids[j];
+  const float *sfx = a.suffix + (int64_t)s * a.suffix_row + (int64_t)h * (D + 2);
   const int n = clamp_len(load_uniform(a.context_lens, s), a.ctx_cap);
   const int raw = load_uniform(a.starts, s);
+  const float m_sfx = load_uniform(sfx, D);
+  float sv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) sv[i] = sfx[lane + kWave * i];
   const int st = raw < 0 ? 0 : min(raw & ~(kDecodeTile - 1), n);
   if (st == 0) return;  // no shared prefix for s: the pass wrote its output
-  const float *sfx = a.suffix + (int64_t)s * a.suffix_row + (int64_t)h * (D + 2);
-  const int64_t chunk_stride = (int64_t)H * kM * (D + 2);  // floats from chunk c to c+1
-  const float *part0 = a.partials + (((int64_t)g * a.chunks * H + h) * kM + j) * (D + 2);
-  const int C = a.chunks;
-  // The common max over the suffix and every chunk, then the sum.
-  const float m_sfx = load_uniform(sfx, D);
+  // The common max over the suffix and every chunk, then the sums.
   float M = m_sfx;
-  for (int c0 = 0; c0 < C; c0 += kU) {
+#pragma unroll
+  for (int u = 0; u < kU; ++u) M = fmaxf(M, mc0[u]);
+  for (int c0 = kU; c0 < C; c0 += kU) {
     float mc[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) mc[u] = c0 + u < C ? load_uniform(part0 + (c0 + u) * chunk_stride, D) : -INFINITY;
@@ -230,34 +248,42 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_combine_ke
   }
   const float mu = (M == -INFINITY) ? 0.f : M;
   const float ws = fast_exp2(m_sfx - mu);  // the suffix partial is normalised: its sum is 1
-  float L = ws;
-  for (int c0 = 0; c0 < C; c0 += kU) {
-    float mc[kU], lc[kU];
+  float L = ws, A[kPer];
+  float e0[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    e0[u] = fast_exp2(mc0[u] - mu);
+    L += lc0[u] * e0[u];
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    A[i] = sv[i] * ws;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) A[i] += v0[u][i] * e0[u];
+  }
+  for (int c0 = kU; c0 < C; c0 += kU) {
+    float mc[kU], lc[kU], v[kU][kPer];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const bool in = c0 + u < C;
       mc[u] = in ? load_uniform(part0 + (c0 + u) * chunk_stride, D) : -INFINITY;
       lc[u] = in ? load_uniform(part0 + (c0 + u) * chunk_stride, D + 1) : 0.f;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) v[u][i] = in ? part0[(c0 + u) * chunk_stride + lane + kWave * i] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) L += lc[u] * fast_exp2(mc[u] - mu);
+    for (int u = 0; u < kU; ++u) {
+      const float e = fast_exp2(mc[u] - mu);
+      L += lc[u] * e;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) A[i] += v[u][i] * e;
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  for (int d = lane; d < D; d += kWave) {
-    float A = sfx[d] * ws;
-    for (int c0 = 0; c0 < C; c0 += kU) {
-      float v[kU], mc[kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const bool in = c0 + u < C;
-        v[u] = in ? part0[(c0 + u) * chunk_stride + d] : 0.f;
-        mc[u] = in ? load_uniform(part0 + (c0 + u) * chunk_stride, D) : -INFINITY;
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) A += v[u] * fast_exp2(mc[u] - mu);
-    }
-    const float o = A * inv;
-    const int64_t idx = ((int64_t)s * H + h) * D + d;
+  for (int i = 0; i < kPer; ++i) {
+    const float o = A[i] * inv;
+    const int64_t idx = ((int64_t)s * H + h) * D + lane + kWave * i;
     if constexpr (T == Dt::F32) reinterpret_cast<float *>(a.out)[idx] = o;
     else if constexpr (T == Dt::F16) reinterpret_cast<uint16_t *>(a.out)[idx] = (uint16_t)f32_to_f16_bits(o);
     else reinterpret_cast<uint16_t *>(a.out)[idx] = (uint16_t)f32_to_bf16_bits(o);
