@@ -89,12 +89,21 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_digest(source: str = "pa_decode.hip") -> str:
-    src = open(os.path.join(ROOT, "paged_kv_cache_109_amd", "csrc", source), "rb").read()
-    return hashlib.sha256(src).hexdigest()[:16]
+# The sources a kernel is built from: the decode partition kernel's walk is
+# in pa_stream.h, its launch and plan in pa_decode.hip.
+DECODE_SOURCES = ("pa_decode.hip", "pa_stream.h")
 
 
-def committed_traffic(profile: str, source: str = "pa_decode.hip"):
+def kernel_source_digest(source=DECODE_SOURCES) -> str:
+    """sha256 (first 16 hex digits) of a kernel's source files, concatenated."""
+    names = (source,) if isinstance(source, str) else source
+    h = hashlib.sha256()
+    for name in names:
+        h.update(open(os.path.join(ROOT, "paged_kv_cache_109_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(profile: str, source=DECODE_SOURCES):
     """HBM bytes per launch of a kernel from its committed rocprofv3 counter
     summary (profiles/<profile>_counters.md), if that summary was taken on
     the current kernel source."""
@@ -106,7 +115,7 @@ def committed_traffic(profile: str, source: str = "pa_decode.hip"):
     m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m or not t or m.group(1) != kernel_source_digest(source):
-        print(f"[bench] {os.path.basename(path)} was taken on another {source} "
+        print(f"[bench] {os.path.basename(path)} was taken on other {'/'.join((source,) if isinstance(source, str) else source)} sources "
               f"({m.group(1) if m else '?'} vs {kernel_source_digest(source)}): traffic = null", file=sys.stderr)
         return None
     return float(t.group(1))

@@ -199,23 +199,39 @@ const void *device_address(const void *p) {
 
 struct SharedGeometry {
   DecodeGeometry dec;
-  int32_t chunks;
-  size_t suffix_off, partials_off, ws_bytes;
+  int32_t chunks;            // piece slots per (group, head)
+  int32_t max_prefix_tiles;  // prefixes are clamped to this many tiles
+  size_t suffix_off, partials_off, pplan_off, ws_bytes;
 };
 
+// The shared-prefix pass splits the prefix tiles into ranges of at least
+// kPrefixMinTiles, so a prefix of T tiles meets at most 1 + ceil((T - 1) /
+// kPrefixMinTiles) of them: that many piece slots per (group, head).
 SharedGeometry shared_geometry(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
                                int32_t max_blocks, int32_t block_size, int64_t workers, int32_t num_groups,
                                int32_t max_prefix_len) {
   SharedGeometry g;
   g.dec = geometry(head_dim, max_context_len, max_blocks, block_size, workers);
   const int64_t prefix_tiles = ceil_div(std::max<int32_t>(max_prefix_len, 0), pa::kDecodeTile);
-  g.chunks = (int32_t)std::max<int64_t>(1, ceil_div(prefix_tiles, pa::kPrefixChunkTiles));
+  g.max_prefix_tiles = (int32_t)prefix_tiles;
+  g.chunks = (int32_t)(prefix_tiles <= 1 ? 1 : 1 + ceil_div(prefix_tiles - 1, pa::kPrefixMinTiles));
   const size_t row = (size_t)head_dim + 2;
   g.suffix_off = round_up(g.dec.ws_bytes, 256);
   g.partials_off = round_up(g.suffix_off + (size_t)num_seqs * num_heads * row * sizeof(float), 256);
-  g.ws_bytes = g.partials_off +
-               (size_t)num_groups * g.chunks * num_heads * pa::kSharedMaxMembers * row * sizeof(float);
+  g.pplan_off = round_up(g.partials_off + (size_t)num_groups * g.chunks * num_heads * pa::kSharedMaxMembers * row *
+                                              sizeof(float),
+                         256);
+  g.ws_bytes = g.pplan_off + ((size_t)pa::kPrefixPlanHeader + 2 * (size_t)num_groups) * sizeof(uint32_t);
   return g;
+}
+
+// Worker waves of a shared-prefix call: as many as the pass kernel holds on
+// the device at once, or split_workers when that is smaller.
+int64_t shared_workers(pa_dtype dtype, int32_t head_dim, int32_t block_size, int32_t split_workers) {
+  const int64_t fit = (int64_t)device_cus() * pa::shared_waves_per_cu(dtype, head_dim, block_size);
+  int64_t w = fit > 0 ? fit : 1;
+  if (split_workers > 0 && split_workers < w) w = split_workers;
+  return w;
 }
 
 }  // namespace
@@ -514,7 +530,7 @@ pa_status pa_paged_attention_decode_shared(void *out, const void *q, const void 
     return fail(PA_ERR_INVALID_ARG, "null group_members or group_prefix");
   if (!aligned16(out) || !aligned16(q)) return fail(PA_ERR_INVALID_ARG, "out and q must be 16-byte aligned");
   if (num_seqs == 0) return ok();
-  const int64_t workers = decode_workers(dtype, head_dim, block_size, split_workers);
+  const int64_t workers = shared_workers(dtype, head_dim, block_size, split_workers);
   const SharedGeometry g = shared_geometry(num_seqs, num_heads, head_dim, max_context_len, max_blocks_per_seq,
                                            block_size, workers, num_groups, max_prefix_len);
   if (!workspace || workspace_bytes < g.ws_bytes)
@@ -531,12 +547,6 @@ pa_status pa_paged_attention_decode_shared(void *out, const void *q, const void 
                              num_blocks, group_members, group_prefix, seq_starts, num_groups, max_prefix_len, s);
     if (st != PA_OK) return st;
   }
-  if (phases & PA_SHARED_OWN) {
-    st = hip_status(pa::launch_decode_partitions(a, dtype, head_dim, block_size, s), "decode partitions");
-    if (st != PA_OK) return st;
-    st = hip_status(pa::launch_decode_reduce(a, dtype, head_dim, s), "decode reduce");
-    if (st != PA_OK) return st;
-  }
   pa::SharedArgs sa;
   sa.out = out;
   sa.q = q;
@@ -548,6 +558,7 @@ pa_status pa_paged_attention_decode_shared(void *out, const void *q, const void 
   sa.members = group_members;
   sa.prefix = group_prefix;
   sa.partials = reinterpret_cast<float *>(ws + g.partials_off);
+  sa.pplan = reinterpret_cast<uint32_t *>(ws + g.pplan_off);
   sa.suffix = a.suffix_out;
   sa.num_blocks = num_blocks;
   sa.num_seqs = num_seqs;
@@ -555,13 +566,20 @@ pa_status pa_paged_attention_decode_shared(void *out, const void *q, const void 
   sa.max_blocks = max_blocks_per_seq;
   sa.num_groups = num_groups;
   sa.chunks = g.chunks;
-  sa.chunk_tiles = pa::kPrefixChunkTiles;
+  sa.max_prefix_tiles = g.max_prefix_tiles;
   sa.ctx_cap = g.dec.ctx_cap;
   sa.suffix_row = a.suffix_row;
   sa.scale_log2 = a.scale_log2;
-  return hip_status(pa::launch_shared_phases(sa, dtype, head_dim, block_size, (phases & PA_SHARED_PREFIX) != 0,
-                                             (phases & PA_SHARED_COMBINE) != 0, s),
-                    "shared prefix");
+  const bool own = (phases & PA_SHARED_OWN) != 0, prefix = (phases & PA_SHARED_PREFIX) != 0;
+  st = hip_status(pa::launch_shared_pass(a, sa, dtype, head_dim, block_size, own, prefix, s), "shared-prefix pass");
+  if (st != PA_OK) return st;
+  if (own) {
+    st = hip_status(pa::launch_decode_reduce(a, dtype, head_dim, s), "decode reduce");
+    if (st != PA_OK) return st;
+  }
+  if (phases & PA_SHARED_COMBINE)
+    return hip_status(pa::launch_shared_combine(sa, dtype, head_dim, s), "shared-prefix combine");
+  return ok();
 }
 
 pa_status pa_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t num_layers,

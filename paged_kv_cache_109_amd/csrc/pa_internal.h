@@ -69,6 +69,9 @@ bool decode_supported(int dtype, int head_dim, int block_size);
 hipError_t launch_decode_partitions(const DecodeArgs &a, int dtype, int head_dim, int block_size,
                                     hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream);
+// The one-workgroup plan of the partition pass (batches above the size the
+// workers plan for themselves).
+hipError_t launch_decode_plan(const DecodeArgs &a, hipStream_t stream);
 
 // The allocation-free decode's workspace: a fixed device array of
 // PA_NOALLOC_SCRATCH_BYTES per device (pa_decode.hip).  Sets *ptr to the
@@ -129,11 +132,13 @@ struct PrefillArgs {
   int64_t new_value_stride;
 };
 
-// Shared-prefix decode (pa_shared.hip): members per group, prefix tiles per
-// work item of the prefix kernel.
+// Shared-prefix decode (pa_shared.hip): members per group.
 constexpr int kSharedMaxMembers = 8;
 static_assert(kSharedMaxMembers == PA_MAX_GROUP_MEMBERS, "group width of the C ABI");
-constexpr int kPrefixChunkTiles = 8;
+// Shortest range of prefix tiles a worker takes (bounds the pieces of a pair).
+constexpr int kPrefixMinTiles = 8;
+// 32-bit words before the per-group entries of the prefix plan.
+constexpr int kPrefixPlanHeader = 4;
 
 struct SharedArgs {
   void *out;                    // [S][H][D]
@@ -145,23 +150,30 @@ struct SharedArgs {
   const int32_t *starts;        // [S] first position of each sequence's own part (0: not in a group)
   const int32_t *members;       // [G][kSharedMaxMembers] sequence ids, -1 past the last member
   const int32_t *prefix;        // [G] shared prefix tokens
-  float *partials;              // [G][chunks][H][kSharedMaxMembers][D + 2]: value sums, max, sum
+  float *partials;              // [G][chunks][H][kSharedMaxMembers][D + 2]: value sums, max, sum per piece
+  uint32_t *pplan;              // [kPrefixPlanHeader + 2G]: prefix tiles, workers used; per group offset, tiles
   const float *suffix;          // [S][H][D + 2]: the decode pass's partials of the own parts
   int64_t num_blocks;
   int32_t num_seqs;
   int32_t num_heads;
   int32_t max_blocks;
   int32_t num_groups;
-  int32_t chunks;               // prefix chunks per group
-  int32_t chunk_tiles;          // tiles per chunk
+  int32_t chunks;               // piece slots per (group, head): the most pieces a prefix pair can be cut into
+  int32_t max_prefix_tiles;     // prefixes are clamped to this many tiles
   int32_t ctx_cap;
   int32_t suffix_row;           // H * (D + 2)
   float scale_log2;
 };
 
 bool shared_supported(int dtype, int head_dim, int block_size);
-hipError_t launch_shared_phases(const SharedArgs &a, int dtype, int head_dim, int block_size, bool prefix,
-                                bool combine, hipStream_t stream);
+// Resident waves per CU of the shared-prefix pass (its worker count per CU).
+int shared_waves_per_cu(int dtype, int head_dim, int block_size);
+// The own positions (own: partitions into d, with d.starts / d.suffix_out set)
+// and the shared prefixes (prefix: pieces into s.partials) in one launch of
+// d.workers worker waves; the reduce and the combine follow.
+hipError_t launch_shared_pass(const DecodeArgs &d, const SharedArgs &s, int dtype, int head_dim, int block_size,
+                              bool own, bool prefix, hipStream_t stream);
+hipError_t launch_shared_combine(const SharedArgs &a, int dtype, int head_dim, hipStream_t stream);
 
 bool prefill_supported(int dtype, int head_dim, int block_size);
 // Shapes whose prefill runs on the matrix-core kernel (the only one with the

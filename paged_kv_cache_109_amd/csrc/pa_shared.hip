@@ -10,14 +10,22 @@
 // them, so a plain decode reads each shared block once per sample.  The
 // softmax splits by position range (the same fact the split-KV pass rests
 // on), so a group's attention is computed as
-//   - the shared prefix [0, P): one wave per (group, head, chunk of prefix
-//     tiles) loads each K/V tile once and folds it into the running state of
-//     every member's query (decode_prefix_kernel, below);
-//   - each member's own positions [P, n): the stream-K decode pass with a
+//   - the shared prefix [0, P): each K/V tile is loaded once and folded into
+//     the running state of every member's query;
+//   - each member's own positions [P, n): the stream-K decode walk with a
 //     per-sequence start, leaving a normalised fp32 partial and its log2
-//     softmax denominator (pa_decode.hip);
+//     softmax denominator (pa_stream.h);
 //   - a merge of the two per (sequence, head) into the output
 //     (decode_combine_kernel, below).
+//
+// One launch does the first two (decode_shared_pass_kernel).  Its worker
+// waves split both streams evenly: worker w of G takes the w-th G-th of the
+// prefix tiles, ordered (group, head, tile), and then the w-th G-th of the
+// own positions' tiles (the partition walk), so every worker gets the same
+// mix and no launch boundary separates the two.  A (group, head) pair of the
+// prefix cut by range boundaries leaves one piece per worker; the combine
+// merges the pieces in order.  Ranges of the prefix stream are at least
+// kPrefixMinTiles long, which bounds the pieces of a pair.
 //
 // Mapping.  As in the decode pass, a K/V row of one token and head is
 // covered by LPT lanes with one 16-byte load each; one wave load covers
@@ -25,37 +33,55 @@
 // prefix tiles are always full (P is a multiple of the tile, within every
 // member's context), so no masking is needed there.  Members' states live
 // in registers (up to kSharedMaxMembers); the lane groups of a wave hold
-// different tokens and are merged at the end of the chunk.
+// different tokens and are merged at the end of each piece.
 
-#include "pa_device.h"
-#include "pa_internal.h"
+#include "pa_stream.h"
 
 namespace pa {
 
-namespace {
+#ifndef PA_SHARED_OWN_DEPTH
+#define PA_SHARED_OWN_DEPTH 4
+#endif
+#ifndef PA_SHARED_PREFIX_DEPTH
+#define PA_SHARED_PREFIX_DEPTH 2
+#endif
+constexpr int kSharedOwnDepth = PA_SHARED_OWN_DEPTH;        // own tiles in flight per wave
+constexpr int kSharedPrefixDepth = PA_SHARED_PREFIX_DEPTH;  // prefix tiles in flight per wave
 
-__device__ __forceinline__ int clamp_len(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
+// Tiles (per head) of group g's shared prefix: the prefix clamped to the
+// first member's context and to the call's bound, in whole tiles; 0 for a
+// group without a valid first member.  Lane-varying g.
+__device__ __forceinline__ uint32_t group_tiles(const SharedArgs &a, int g) {
+  const int lead = a.members[(int64_t)g * kSharedMaxMembers];
+  if (lead < 0 || lead >= a.num_seqs) return 0u;
+  const int n0 = clip_ctx(a.context_lens[lead], a.ctx_cap);
+  const int p = a.prefix[g];
+  const int t = (p < 0 ? 0 : (p > n0 ? n0 : p)) / kDecodeTile;
+  return (uint32_t)(t < a.max_prefix_tiles ? t : a.max_prefix_tiles);
+}
 
-}  // namespace
+// The same for a wave-uniform g (scalar loads).
+__device__ __forceinline__ uint32_t group_tiles_uniform(const SharedArgs &a, int g) {
+  const int lead = load_uniform(a.members, (int64_t)g * kSharedMaxMembers);
+  if (lead < 0 || lead >= a.num_seqs) return 0u;
+  const int n0 = clip_ctx(load_uniform(a.context_lens, lead), a.ctx_cap);
+  const int p = load_uniform(a.prefix, g);
+  const int t = (p < 0 ? 0 : (p > n0 ? n0 : p)) / kDecodeTile;
+  return (uint32_t)(t < a.max_prefix_tiles ? t : a.max_prefix_tiles);
+}
 
-constexpr int kPrefixDepth = 2;  // tiles in flight per wave
-
-template <Dt T, int D, int B>
-__global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_prefix_kernel(SharedArgs a) {
+// Fold tiles [t0, t1) of group g's prefix, head h, into the state of every
+// member's query and store each member's (value sum, max, sum) as piece c of
+// the pair.
+template <Dt T, int D, int B, int kDepthP>
+__device__ __forceinline__ void prefix_piece(const SharedArgs &a, int g, int h, int t0, int t1, uint32_t c) {
   using R = RowShape<T, D, kDecodeTile>;
   constexpr int kM = kSharedMaxMembers;
   static_assert(B % kDecodeTile == 0, "a prefix tile must lie in one block");
   const int lane = threadIdx.x % kWave;
-  const int w = blockIdx.x * kDecodeWavesPerGroup + wave_id_uniform();
   const int H = a.num_heads;
-  const int h = w % H;
-  const int c = (w / H) % a.chunks;
-  const int g = w / (H * a.chunks);
-  if (g >= a.num_groups) return;
 
-  // Members (a leading run of valid sequence ids) and the group's prefix
-  // tiles, clamped to the first member's context so that every table entry
-  // read lies inside its row.
+  // Members: a leading run of valid sequence ids.
   int sm[kM];
   int nm = 0;
 #pragma unroll
@@ -64,15 +90,9 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_prefix_ker
     sm[j] = s;
     if (nm == j && s >= 0 && s < a.num_seqs) nm = j + 1;
   }
+  if (nm == 0 || c >= (uint32_t)a.chunks) return;
   float *dst = a.partials + (((int64_t)g * a.chunks + c) * H + h) * kM * (D + 2);
-  if (nm == 0) return;
   const int leader = sm[0];
-  int prefix = load_uniform(a.prefix, g);
-  const int n0 = clamp_len(load_uniform(a.context_lens, leader), a.ctx_cap);
-  prefix = prefix < 0 ? 0 : (prefix > n0 ? n0 : prefix);
-  const int tiles = prefix / kDecodeTile;
-  const int t0 = c * a.chunk_tiles;
-  const int t1 = min(tiles, t0 + a.chunk_tiles);
 
   const int grp = lane / R::kLPT, col = lane % R::kLPT;
   const char *kbase = reinterpret_cast<const char *>(a.k_cache);
@@ -97,11 +117,11 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_prefix_ker
     for (int e = 0; e < R::kFE; ++e) acc[j][e] = 0.f;
   }
 
-  // Loads of tile t into slot d; t past the range (or a block outside the
+  // Loads of tile t into slot d; t past the piece (or a block outside the
   // pool) loads row 0 of block 0 and is marked dead, so that every issue is
   // the same instruction sequence and the waits stay exact.
-  uint4 kb[kPrefixDepth][R::kNI], vb[kPrefixDepth][R::kNI];
-  bool okb[kPrefixDepth];
+  uint4 kb[kDepthP][R::kNI], vb[kDepthP][R::kNI];
+  bool okb[kDepthP];
   auto issue = [&](int d, int t) {
     int32_t phys = -1;
     if (t < t1) {
@@ -146,12 +166,12 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_prefix_ker
   };
 
 #pragma unroll
-  for (int d = 0; d < kPrefixDepth; ++d) issue(d, t0 + d);
-  for (int t = t0; t < t1; t += kPrefixDepth) {
+  for (int d = 0; d < kDepthP; ++d) issue(d, t0 + d);
+  for (int t = t0; t < t1; t += kDepthP) {
 #pragma unroll
-    for (int d = 0; d < kPrefixDepth; ++d) {
+    for (int d = 0; d < kDepthP; ++d) {
       if (t + d < t1) consume(d);
-      issue(d, t + d + kPrefixDepth);
+      issue(d, t + d + kDepthP);
     }
   }
 
@@ -184,18 +204,111 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_prefix_ker
   }
 }
 
-// out[s][h] for member j of group g: the prefix chunks' partials and the
-// pass's partial of s's own positions, rescaled to a common max.  One wave
-// per (group, member, head); lane l holds dimensions l, l+64, ...  The work
-// is a few small reads, so their latency is what counts.  The partials of
-// the first kU chunks depend only on (g, j, h), so they are loaded before
-// the member ids, and the member's own row right after them: two round trips
-// to memory in the usual case of at most kU chunks.  The sums run over the
-// suffix and then the chunks in order, whichever loop a chunk's loads are in.
+// Worker w's share of the prefix stream: every (group g, head h, tile t),
+// ordered g, h, t, split over Gp <= G workers in equal ranges of at least
+// kPrefixMinTiles tiles.  Worker 0 publishes the stream's size and split and
+// every group's offset and tiles in a.pplan for the combine.
+template <Dt T, int D, int B, int kDepthP>
+__device__ __forceinline__ void prefix_worker(const SharedArgs &a, uint32_t w, uint32_t G) {
+  const int lane = threadIdx.x % kWave;
+  const int NG = a.num_groups;
+  const uint64_t H = (uint64_t)a.num_heads;
+  uint32_t per_head = 0;
+  for (int c0 = 0; c0 < NG; c0 += kWave) {
+    const int g = c0 + lane;
+    const uint32_t tg = g < NG ? group_tiles(a, g) : 0u;
+    per_head += __builtin_amdgcn_readlane(wave_inclusive_scan(tg), kWave - 1);
+  }
+  const uint32_t TP = (uint32_t)(per_head * H);
+  uint32_t Gp = TP / kPrefixMinTiles;
+  Gp = Gp < 1u ? 1u : (Gp > G ? G : Gp);
+  const bool writer = w == 0;
+  if (writer && lane == 0) {
+    a.pplan[0] = TP;
+    a.pplan[1] = Gp;
+  }
+  const bool worker = TP > 0 && w < Gp;
+  if (!worker && !writer) return;
+  const uint32_t p0 = worker ? range_begin(w, TP, Gp) : 0u, p1 = worker ? range_begin(w + 1, TP, Gp) : 0u;
+
+  // The group holding p0 (the first with tiles whose end passes p0); worker
+  // 0 also stores every group's offset and tiles.
+  int g_at = -1;
+  uint32_t off_at = 0, tg_at = 0, base = 0;
+  for (int c0 = 0; c0 < NG; c0 += kWave) {
+    const int g = c0 + lane;
+    const uint32_t tg = g < NG ? group_tiles(a, g) : 0u;
+    const uint32_t incl = wave_inclusive_scan(tg);
+    const uint32_t off = base + incl - tg;
+    if (writer && g < NG) {
+      a.pplan[kPrefixPlanHeader + 2 * g] = off;
+      a.pplan[kPrefixPlanHeader + 2 * g + 1] = tg;
+    }
+    if (worker && g_at < 0) {
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(tg > 0 && (uint64_t)(off + tg) * H > p0);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        g_at = c0 + l;
+        off_at = __builtin_amdgcn_readlane(off, l);
+        tg_at = __builtin_amdgcn_readlane(tg, l);
+      }
+    }
+    base += __builtin_amdgcn_readlane(incl, kWave - 1);
+    if (!writer && g_at >= 0) break;
+  }
+  if (!worker || g_at < 0) return;
+
+  int g = g_at;
+  uint32_t off = off_at, tg = tg_at;
+  const uint32_t local = p0 - (uint32_t)(off * H);
+  int h = (int)(local / tg), t = (int)(local % tg);
+  uint32_t p = p0;
+  for (;;) {
+    const uint32_t pair_start = (uint32_t)(off * H) + (uint32_t)h * tg;
+    const uint32_t left = p1 - p;
+    const int t_end = (uint32_t)(tg - t) < left ? (int)tg : t + (int)left;
+    prefix_piece<T, D, B, kDepthP>(a, g, h, t, t_end, w - first_worker(pair_start, TP, Gp));
+    p += (uint32_t)(t_end - t);
+    if (p >= p1) break;
+    t = 0;
+    if (++h == a.num_heads) {
+      h = 0;
+      off += tg;
+      do {
+        if (++g >= NG) return;  // not reached: p < p1 <= TP
+        tg = group_tiles_uniform(a, g);
+      } while (tg == 0);
+    }
+  }
+}
+
+constexpr int kPassOwn = 1;
+constexpr int kPassPrefix = 2;
+
+// The own positions (what & kPassOwn) and the shared prefixes (what &
+// kPassPrefix) of a shared-prefix decode in one launch; every wave of the
+// grid is a worker of both streams (a.workers of them).
+template <Dt T, int D, int B>
+__global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_shared_pass_kernel(DecodeArgs a, SharedArgs s,
+                                                                                         int what) {
+  const uint32_t w = blockIdx.x * kDecodeWavesPerGroup + wave_id_uniform();
+  if (what & kPassPrefix) prefix_worker<T, D, B, kSharedPrefixDepth>(s, w, (uint32_t)a.workers);
+  if (what & kPassOwn) partition_worker<T, D, B, false, kSharedOwnDepth>(a, w);
+}
+
+// out[s][h] for member j of group g: the pieces of the (g, h) prefix pair and
+// the pass's partial of s's own positions, rescaled to a common max.  One
+// wave per (group, member, head); lane l holds dimensions l, l+64, ...  The
+// work is a few small reads, so their latency is what counts.  The first kU
+// piece slots depend only on (g, j, h), so they are loaded together with the
+// prefix plan before the member ids (and used only for the pieces the plan
+// says exist), and the member's own row right after them: two round trips to
+// memory in the usual case of at most kU pieces.  The sums run over the
+// suffix and then the pieces in order, whichever loop a piece's loads are in.
 template <Dt T, int D>
 __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_combine_kernel(SharedArgs a) {
   constexpr int kM = kSharedMaxMembers;
-  constexpr int kU = 4;                   // chunks loaded up front (and per later batch)
+  constexpr int kU = 4;                   // pieces loaded up front (and per later batch)
   constexpr int kPer = D / kWave;         // dimensions per lane
   static_assert(D % kWave == 0, "head_dim is whole waves");
   const int lane = threadIdx.x % kWave;
@@ -206,8 +319,11 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_combine_ke
   const int g = w / (H * kM);
   if (g >= a.num_groups) return;
   const int C = a.chunks;
-  const int64_t chunk_stride = (int64_t)H * kM * (D + 2);  // floats from chunk c to c+1
+  const int64_t chunk_stride = (int64_t)H * kM * (D + 2);  // floats from piece slot c to c+1
   const float *part0 = a.partials + (((int64_t)g * C * H + h) * kM + j) * (D + 2);
+  const uint32_t TP = load_uniform(a.pplan, 0), Gp = load_uniform(a.pplan, 1);
+  const uint32_t off = load_uniform(a.pplan, kPrefixPlanHeader + 2 * g);
+  const uint32_t tg = load_uniform(a.pplan, kPrefixPlanHeader + 2 * g + 1);
   float mc0[kU], lc0[kU], v0[kU][kPer];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
@@ -217,8 +333,24 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_combine_ke
 #pragma unroll
     for (int i = 0; i < kPer; ++i) v0[u][i] = in ? part0[u * chunk_stride + lane + kWave * i] : 0.f;
   }
+  // Pieces of the pair: one per worker whose prefix range meets it.
+  int np = 0;
+  if (tg > 0) {
+    const uint32_t ps = off * (uint32_t)H + (uint32_t)h * tg;
+    np = (int)(first_worker(ps + tg - 1, TP, Gp) - first_worker(ps, TP, Gp)) + 1;
+    np = np < C ? np : C;
+  }
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    if (u >= np) {
+      mc0[u] = -INFINITY;
+      lc0[u] = 0.f;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) v0[u][i] = 0.f;
+    }
+  }
   // Member j exists only inside the leading run of valid ids (as the prefix
-  // kernel counts them).
+  // pieces count them).
   int ids[kM];
 #pragma unroll
   for (int i = 0; i < kM; ++i) ids[i] = load_uniform(a.members, (int64_t)g * kM + i);
@@ -227,7 +359,7 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_combine_ke
     if (i <= j && (ids[i] < 0 || ids[i] >= a.num_seqs)) return;
   const int s = ids[j];
   const float *sfx = a.suffix + (int64_t)s * a.suffix_row + (int64_t)h * (D + 2);
-  const int n = clamp_len(load_uniform(a.context_lens, s), a.ctx_cap);
+  const int n = clip_ctx(load_uniform(a.context_lens, s), a.ctx_cap);
   const int raw = load_uniform(a.starts, s);
   const float m_sfx = load_uniform(sfx, D);
   float sv[kPer];
@@ -235,14 +367,14 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_combine_ke
   for (int i = 0; i < kPer; ++i) sv[i] = sfx[lane + kWave * i];
   const int st = raw < 0 ? 0 : min(raw & ~(kDecodeTile - 1), n);
   if (st == 0) return;  // no shared prefix for s: the pass wrote its output
-  // The common max over the suffix and every chunk, then the sums.
+  // The common max over the suffix and every piece, then the sums.
   float M = m_sfx;
 #pragma unroll
   for (int u = 0; u < kU; ++u) M = fmaxf(M, mc0[u]);
-  for (int c0 = kU; c0 < C; c0 += kU) {
+  for (int c0 = kU; c0 < np; c0 += kU) {
     float mc[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) mc[u] = c0 + u < C ? load_uniform(part0 + (c0 + u) * chunk_stride, D) : -INFINITY;
+    for (int u = 0; u < kU; ++u) mc[u] = c0 + u < np ? load_uniform(part0 + (c0 + u) * chunk_stride, D) : -INFINITY;
 #pragma unroll
     for (int u = 0; u < kU; ++u) M = fmaxf(M, mc[u]);
   }
@@ -261,11 +393,11 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_combine_ke
 #pragma unroll
     for (int u = 0; u < kU; ++u) A[i] += v0[u][i] * e0[u];
   }
-  for (int c0 = kU; c0 < C; c0 += kU) {
+  for (int c0 = kU; c0 < np; c0 += kU) {
     float mc[kU], lc[kU], v[kU][kPer];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const bool in = c0 + u < C;
+      const bool in = c0 + u < np;
       mc[u] = in ? load_uniform(part0 + (c0 + u) * chunk_stride, D) : -INFINITY;
       lc[u] = in ? load_uniform(part0 + (c0 + u) * chunk_stride, D + 1) : 0.f;
 #pragma unroll
@@ -295,39 +427,65 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_combine_ke
 namespace {
 
 template <Dt T, int D, int B>
-hipError_t launch_prefix_tdb(const SharedArgs &a, hipStream_t st) {
-  const int64_t items = (int64_t)a.num_groups * a.chunks * a.num_heads;
-  const unsigned groups = (unsigned)((items + kDecodeWavesPerGroup - 1) / kDecodeWavesPerGroup);
-  hipLaunchKernelGGL((decode_prefix_kernel<T, D, B>), dim3(groups), dim3(kDecodeWavesPerGroup * kWave), 0, st, a);
+int pass_waves() {
+  static const int v = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_shared_pass_kernel<T, D, B>,
+                                                     kDecodeWavesPerGroup * kWave, 0) != hipSuccess ||
+        nb < 1)
+      nb = 1;
+    return nb * kDecodeWavesPerGroup;
+  }();
+  return v;
+}
+
+template <Dt T, int D, int B>
+hipError_t launch_pass_tdb(const DecodeArgs &a, const SharedArgs &s, int what, hipStream_t st) {
+  const unsigned groups = (unsigned)((a.workers + kDecodeWavesPerGroup - 1) / kDecodeWavesPerGroup);
+  hipLaunchKernelGGL((decode_shared_pass_kernel<T, D, B>), dim3(groups), dim3(kDecodeWavesPerGroup * kWave), 0, st,
+                     a, s, what);
   return hipGetLastError();
 }
 
-template <Dt T, int D>
-hipError_t launch_prefix_td(const SharedArgs &a, int B, hipStream_t st) {
-  switch (B) {
-    case 16: return launch_prefix_tdb<T, D, 16>(a, st);
-    case 32: return launch_prefix_tdb<T, D, 32>(a, st);
-    case 64: return launch_prefix_tdb<T, D, 64>(a, st);
+#define PA_SHARED_DISPATCH(FN, ...)                                   \
+  switch (D) {                                                        \
+    case 64:                                                          \
+      switch (B) {                                                    \
+        case 16: return FN<T, 64, 16>(__VA_ARGS__);                   \
+        case 32: return FN<T, 64, 32>(__VA_ARGS__);                   \
+        case 64: return FN<T, 64, 64>(__VA_ARGS__);                   \
+      }                                                               \
+      break;                                                          \
+    case 128:                                                         \
+      switch (B) {                                                    \
+        case 16: return FN<T, 128, 16>(__VA_ARGS__);                  \
+        case 32: return FN<T, 128, 32>(__VA_ARGS__);                  \
+        case 64: return FN<T, 128, 64>(__VA_ARGS__);                  \
+      }                                                               \
+      break;                                                          \
   }
+
+template <Dt T>
+int pass_waves_t(int D, int B) {
+  PA_SHARED_DISPATCH(pass_waves)
+  return 0;
+}
+
+template <Dt T>
+hipError_t launch_pass_t(const DecodeArgs &a, const SharedArgs &s, int D, int B, int what, hipStream_t st) {
+  PA_SHARED_DISPATCH(launch_pass_tdb, a, s, what, st)
   return hipErrorInvalidValue;
 }
 
 template <Dt T>
-hipError_t launch_shared_t(const SharedArgs &a, int D, int B, bool prefix, bool combine, hipStream_t st) {
+hipError_t launch_combine_t(const SharedArgs &a, int D, hipStream_t st) {
   const int64_t items = (int64_t)a.num_groups * kSharedMaxMembers * a.num_heads;
   const dim3 grid((unsigned)((items + kDecodeWavesPerGroup - 1) / kDecodeWavesPerGroup));
   const dim3 block(kDecodeWavesPerGroup * kWave);
-  if (D != 64 && D != 128) return hipErrorInvalidValue;
-  if (prefix) {
-    const hipError_t e = D == 64 ? launch_prefix_td<T, 64>(a, B, st) : launch_prefix_td<T, 128>(a, B, st);
-    if (e != hipSuccess) return e;
-  }
-  if (combine) {
-    if (D == 64) hipLaunchKernelGGL((decode_combine_kernel<T, 64>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_combine_kernel<T, 128>), grid, block, 0, st, a);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  if (D == 64) hipLaunchKernelGGL((decode_combine_kernel<T, 64>), grid, block, 0, st, a);
+  else if (D == 128) hipLaunchKernelGGL((decode_combine_kernel<T, 128>), grid, block, 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -337,13 +495,37 @@ bool shared_supported(int dtype, int head_dim, int block_size) {
          (block_size == 16 || block_size == 32 || block_size == 64);
 }
 
-hipError_t launch_shared_phases(const SharedArgs &a, int dtype, int head_dim, int block_size, bool prefix,
-                                bool combine, hipStream_t stream) {
-  if (a.num_groups == 0 || (!prefix && !combine)) return hipSuccess;
+int shared_waves_per_cu(int dtype, int head_dim, int block_size) {
   switch (static_cast<Dt>(dtype)) {
-    case Dt::F32: return launch_shared_t<Dt::F32>(a, head_dim, block_size, prefix, combine, stream);
-    case Dt::F16: return launch_shared_t<Dt::F16>(a, head_dim, block_size, prefix, combine, stream);
-    case Dt::BF16: return launch_shared_t<Dt::BF16>(a, head_dim, block_size, prefix, combine, stream);
+    case Dt::F32: return pass_waves_t<Dt::F32>(head_dim, block_size);
+    case Dt::F16: return pass_waves_t<Dt::F16>(head_dim, block_size);
+    case Dt::BF16: return pass_waves_t<Dt::BF16>(head_dim, block_size);
+  }
+  return 0;
+}
+
+hipError_t launch_shared_pass(const DecodeArgs &a, const SharedArgs &s, int dtype, int head_dim, int block_size,
+                              bool own, bool prefix, hipStream_t stream) {
+  if (!own && !prefix) return hipSuccess;
+  if (own && a.num_seqs > kSelfPlanSeqs) {
+    const hipError_t e = launch_decode_plan(a, stream);
+    if (e != hipSuccess) return e;
+  }
+  const int what = (own ? kPassOwn : 0) | (prefix ? kPassPrefix : 0);
+  switch (static_cast<Dt>(dtype)) {
+    case Dt::F32: return launch_pass_t<Dt::F32>(a, s, head_dim, block_size, what, stream);
+    case Dt::F16: return launch_pass_t<Dt::F16>(a, s, head_dim, block_size, what, stream);
+    case Dt::BF16: return launch_pass_t<Dt::BF16>(a, s, head_dim, block_size, what, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_shared_combine(const SharedArgs &a, int dtype, int head_dim, hipStream_t stream) {
+  if (a.num_groups == 0) return hipSuccess;
+  switch (static_cast<Dt>(dtype)) {
+    case Dt::F32: return launch_combine_t<Dt::F32>(a, head_dim, stream);
+    case Dt::F16: return launch_combine_t<Dt::F16>(a, head_dim, stream);
+    case Dt::BF16: return launch_combine_t<Dt::BF16>(a, head_dim, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -135,3 +135,46 @@ def test_phases_on_two_streams_equal_the_single_call():
         side.wait_stream(main)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), one.view(torch.int16)), f"repeat {rep}"
+
+
+@pytest.mark.parametrize("workers", [1, 2, 3, 7, 64, 4096])
+def test_prefix_stream_split_over_any_number_of_workers(workers):
+    """The prefix tiles of every (group, head) are split over the workers in
+    equal ranges: one worker walks every pair whole, a few cut pairs into
+    several pieces, many are held to the shortest range.  Every split gives
+    the oracle's result."""
+    spec = SPEC + [(200, [3, 1, 2]), (96, [0, 7])]
+    q, k, v, tables, lens, groups = build("f16", 128, 16, spec, singles=[5, 33], seed=workers)
+    ref = oracle.decode(q, k, v, tables, lens, D_SCALE[128], "f16")
+    out, gp = run_shared(q, k, v, tables, lens, groups, 16, "f16", workers)
+    assert gp.max() >= 192
+    check_attention(out, ref, "f16", f"shared decode, {workers} workers")
+
+
+def test_many_groups_with_and_without_prefix_tiles():
+    """More groups than a wave has lanes (the prefix plan scans them in
+    rounds of 64), with prompts shorter than one tile (no shared tile at
+    all) between groups that share several."""
+    rng = np.random.default_rng(5)
+    spec = [(int(p), [int(t) for t in rng.integers(0, 9, size=int(n))])
+            for p, n in zip(rng.choice([3, 12, 16, 21, 40, 64, 90], size=150), rng.integers(2, 5, size=150))]
+    q, k, v, tables, lens, groups = build("bf16", 64, 16, spec, singles=[2, 17], seed=5, H=2)
+    ref = oracle.decode(q, k, v, tables, lens, D_SCALE[64], "bf16")
+    for workers in (0, 9):
+        out, gp = run_shared(q, k, v, tables, lens, groups, 16, "bf16", workers)
+        assert (gp == 0).any() and (gp >= 64).any()
+        check_attention(out, ref, "bf16", f"150 groups, workers={workers}")
+
+
+def test_shared_decode_above_the_self_planned_batch():
+    """More than 1024 sequences: the own positions are planned by the plan
+    kernel before the pass."""
+    rng = np.random.default_rng(11)
+    spec = [(48, [1, 2, 3, 0]) for _ in range(30)]
+    singles = [int(n) for n in rng.integers(1, 40, size=1000)]
+    q, k, v, tables, lens, groups = build("f16", 64, 16, spec, singles=singles, seed=11, H=2)
+    assert len(lens) > 1024
+    ref = oracle.decode(q, k, v, tables, lens, D_SCALE[64], "f16")
+    out, gp = run_shared(q, k, v, tables, lens, groups, 16, "f16")
+    assert (gp == 48).all()
+    check_attention(out, ref, "f16", f"{len(lens)} sequences")
