@@ -337,7 +337,10 @@ pa_status pa_paged_attention_decode_reduce(void *out, const int32_t *context_len
  * of several responses).  Attention splits by position range (review
  * section 4.1), so the call computes, per (sequence, head): the shared
  * prefix [0, P) for all members of a group at once, each member's own
- * positions [P, n) with the stream-K pass, and their merge.
+ * positions [P, n) with the stream-K pass, and their merge.  The first two
+ * share one launch whose worker waves split both the prefix tiles and the
+ * own tiles evenly; the own positions' cut pairs and the merge are two more
+ * launches.
  *
  *  group_members  device int32 [num_groups][PA_MAX_GROUP_MEMBERS]: the
  *                 members of each group, a leading run of sequence ids,
@@ -356,11 +359,13 @@ pa_status pa_paged_attention_decode_reduce(void *out, const int32_t *context_len
  *                 (each sequence's own positions: the stream-K pass and its
  *                 fix-up), PA_SHARED_PREFIX (the groups' shared prefixes),
  *                 PA_SHARED_COMBINE (the merge into out); PA_SHARED_ALL runs
- *                 them in order on `stream`.  OWN and PREFIX read disjoint
- *                 data and write disjoint parts of the workspace, so a caller
- *                 may enqueue them on two streams to run at once; COMBINE
- *                 must follow both (e.g. after an event join).  Every call of
- *                 one decode passes the same arguments and workspace.
+ *                 them on `stream`, OWN and PREFIX in one launch.  OWN and
+ *                 PREFIX read disjoint data and write disjoint parts of the
+ *                 workspace, so a caller may also enqueue them as separate
+ *                 calls on two streams; COMBINE must follow both (e.g. after
+ *                 an event join).  Every call of one decode passes the same
+ *                 arguments, split_workers and workspace; the results are
+ *                 then the same bits however the steps are enqueued.
  * Other arguments as for pa_paged_attention_decode.  block_size 16, 32 or
  * 64 (PA_ERR_UNSUPPORTED otherwise).  The group description is checked
  * against the tables only under PA_DEBUG_VALIDATE=1 (that needs device
