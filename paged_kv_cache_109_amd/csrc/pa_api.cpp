@@ -91,7 +91,7 @@ DecodeGeometry geometry(int32_t head_dim, int32_t max_context_len, int32_t max_b
   if (max_blocks >= 0 && (int64_t)max_blocks * block_size < cap) cap = (int64_t)max_blocks * block_size;
   g.ctx_cap = (int32_t)(cap < 0 ? 0 : cap);
   g.workers = workers;
-  g.plan_bytes = round_up(((size_t)pa::kPlanHeader + 2 * (size_t)workers) * sizeof(uint32_t), 256);
+  g.plan_bytes = round_up(((size_t)pa::kPlanHeader + pa::kPlanWords * (size_t)workers) * sizeof(uint32_t), 256);
   g.ws_bytes = g.plan_bytes + (size_t)workers * 2 * ((size_t)head_dim + 2) * sizeof(float);
   return g;
 }

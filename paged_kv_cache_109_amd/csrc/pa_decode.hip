@@ -52,8 +52,9 @@ constexpr int kPlanThreads = 1024;
 // Plan for batches of more than kSelfPlanSeqs sequences (smaller batches are
 // planned by the worker waves themselves, see self_plan).  One workgroup.
 // plan[0] = total tiles T, plan[1] = G = min(launched workers, T), and for
-// every worker w < G the (s | h << 16, t) of its first tile at
-// plan[kPlanHeader + 2w]; zeroes the outputs of empty sequences.
+// every worker w < G the (s | h << 16, t) of its first tile and the tiles of
+// that pair at plan[kPlanHeader + kPlanWords*w]; zeroes the outputs of empty
+// sequences.
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a) {
   __shared__ uint32_t scan[kPlanThreads];
   const int tid = threadIdx.x;
@@ -89,8 +90,9 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
       const uint64_t w_hi = ((uint64_t)c_next * G + total - 1) / total;
       for (uint64_t w = w_lo; w < w_hi; ++w) {
         const uint32_t local = range_begin((uint32_t)w, total, G) - c;
-        a.plan[kPlanHeader + 2 * w] = (uint32_t)s | ((local / ts) << 16);
-        a.plan[kPlanHeader + 2 * w + 1] = local % ts;
+        a.plan[kPlanHeader + kPlanWords * w] = (uint32_t)s | ((local / ts) << 16);
+        a.plan[kPlanHeader + kPlanWords * w + 1] = local % ts;
+        a.plan[kPlanHeader + kPlanWords * w + 2] = ts;
       }
     } else {
       empty_rows(a, s, 0, 1);
@@ -116,7 +118,6 @@ __device__ __forceinline__ void merge_fragments(const DecodeArgs &a, uint32_t wa
   };
   constexpr int kPer = (D + kWave - 1) / kWave;  // head dimensions per lane
   const uint32_t cnt = wb - wa + 1;
-  const int n = clip_ctx(a.context_lens[s], a.ctx_cap);
   float M = -INFINITY, L = 0.f, A[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) A[j] = 0.f;
@@ -161,7 +162,7 @@ __device__ __forceinline__ void merge_fragments(const DecodeArgs &a, uint32_t wa
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   float *part = nullptr;
-  if (a.starts && to_partial(a, start_of(a.starts[s], n)))
+  if (a.starts && to_partial(a, start_of(a.starts[s], clip_ctx(a.context_lens[s], a.ctx_cap))))
     part = a.suffix_out + (int64_t)s * a.suffix_row + (int64_t)h * (D + 2);
   const int64_t out_row = ((int64_t)s * a.num_heads + h) * D;
 #pragma unroll
@@ -233,16 +234,18 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_reduce_ker
   }
   // Every worker wave v that the loop below visits has a non-empty range
   // (the plan never uses more workers than tiles) and wrote its fragment.
-  const uint32_t G = a.plan[1];
+  // This wave's plan words are read together with G, at an index clamped to
+  // the plan (the grid may hold a few waves more than workers).
   const uint32_t w = blockIdx.x * kDecodeWavesPerGroup + wave_id_uniform();
+  const uint32_t wc = w < (uint32_t)a.workers ? w : (uint32_t)a.workers - 1u;
+  const uint32_t G = load_uniform(a.plan, 1), total = load_uniform(a.plan, 0);
+  const uint32_t sh = load_uniform(a.plan, kPlanHeader + kPlanWords * wc);
+  const uint32_t t = load_uniform(a.plan, kPlanHeader + kPlanWords * wc + 1);
+  const uint32_t nt = load_uniform(a.plan, kPlanHeader + kPlanWords * wc + 2);
   if (w >= G) return;
-  const uint32_t total = a.plan[0];
   const uint32_t g0 = range_begin(w, total, G), g1 = range_begin(w + 1, total, G);
-  const uint32_t sh = a.plan[kPlanHeader + 2 * w];
   const int s = (int)(sh & 0xffffu), h = (int)(sh >> 16);
-  const uint32_t t = a.plan[kPlanHeader + 2 * w + 1];
   if (t == 0) return;  // the pair starts at g0: not cut at the front of this range
-  const uint32_t nt = (uint32_t)pass_tiles(a, s, clip_ctx(a.context_lens[s], a.ctx_cap));
   const uint32_t pair_start = g0 - t;
   if (pair_start + nt > g1) return;  // continues past this range: a later worker merges it
   merge_fragments<T, D>(a, first_worker(pair_start, total, G), w, s, h);

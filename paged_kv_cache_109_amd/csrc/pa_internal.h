@@ -18,7 +18,7 @@ pa_status record_ok();
 // Arguments of the decode passes.  Pointers are device pointers.
 struct DecodeArgs {
   void *out;            // [S][H][D] dtype
-  uint32_t *plan;       // [kPlanHeader + 2*workers]: total tiles, workers used, per-worker start
+  uint32_t *plan;       // [kPlanHeader + kPlanWords*workers]: total tiles, workers used, per-worker start
   float *frags;         // [workers][2][D + 2]: fragment value sums, then m (log2 units), l
   const void *q;        // [S][H][D]
   const void *k_cache;  // [N][H][B][D]
@@ -53,8 +53,10 @@ struct DecodeArgs {
   int64_t new_value_stride;
 };
 
-// 32-bit words before the per-worker starts in the plan.
+// 32-bit words before the per-worker starts in the plan, and words per
+// worker: (s | h << 16, t) of its first tile and the tiles of that pair.
 constexpr int kPlanHeader = 4;
+constexpr int kPlanWords = 3;
 // Tokens a decode wave processes per step (one tile).
 constexpr int kDecodeTile = 16;
 // Independent worker waves packed into one workgroup.

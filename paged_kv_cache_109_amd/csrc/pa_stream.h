@@ -128,7 +128,8 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 // one inclusive scan over the lanes' tile counts places every lane's run in
 // the stream; the lane whose run holds tile g0 is found with a ballot and its
 // k sequences are walked on the scalar unit.  Wave 0 also publishes T and G
-// in plan[0..1]; every worker stores its start for the fix-up, and zeroes
+// in plan[0..1]; every worker stores its start (and the tiles of the pair
+// there) for the fix-up, and zeroes
 // the outputs of the empty sequences s with s % G == w.  Returns false if
 // the wave has no work.
 __device__ __forceinline__ bool self_plan(const DecodeArgs &a, uint32_t w, uint32_t &total, uint32_t &G,
@@ -191,8 +192,9 @@ __device__ __forceinline__ bool self_plan(const DecodeArgs &a, uint32_t w, uint3
       h0 = (int)(local / ts);
       t0 = (int)(local % ts);
       if (lane == 0) {
-        a.plan[kPlanHeader + 2 * w] = (uint32_t)s0 | ((uint32_t)h0 << 16);
-        a.plan[kPlanHeader + 2 * w + 1] = (uint32_t)t0;
+        a.plan[kPlanHeader + kPlanWords * w] = (uint32_t)s0 | ((uint32_t)h0 << 16);
+        a.plan[kPlanHeader + kPlanWords * w + 1] = (uint32_t)t0;
+        a.plan[kPlanHeader + kPlanWords * w + 2] = ts;
       }
       return true;
     }
@@ -207,10 +209,10 @@ __device__ __forceinline__ uint32_t first_worker(uint32_t pair_start, uint32_t t
   return (uint32_t)((((uint64_t)pair_start + 1) * G + total - 1) / total) - 1;
 }
 
-
-// kAppend: each sequence's newest token (position n - 1) is read from
-// a.new_key / a.new_value instead of the cache.  The pass only reads; the
-// rows are stored into the cache by the reduce pass, after every read of
+// One worker wave's share of the partition pass.  kAppend: each sequence's
+// newest token (position n - 1) is read from a.new_key / a.new_value instead
+// of the cache.  The pass only reads; the rows are stored into the cache by
+// the reduce pass, after every read of this launch.
 template <Dt T, int D, int B, bool kAppend, int kDepthT>
 __device__ __forceinline__ void partition_worker(const DecodeArgs &a, uint32_t w) {
   using R = RowShape<T, D, kDecodeTile>;
@@ -223,10 +225,10 @@ __device__ __forceinline__ void partition_worker(const DecodeArgs &a, uint32_t w
     G = load_uniform(a.plan, 1);
     if (w >= G) return;
     total = load_uniform(a.plan, 0);
-    const uint32_t sh = load_uniform(a.plan, kPlanHeader + 2 * w);
+    const uint32_t sh = load_uniform(a.plan, kPlanHeader + kPlanWords * w);
     ic.s = (int)(sh & 0xffffu);
     ic.h = (int)(sh >> 16);
-    ic.t = (int)load_uniform(a.plan, kPlanHeader + 2 * w + 1);
+    ic.t = (int)load_uniform(a.plan, kPlanHeader + kPlanWords * w + 1);
   }
   const uint32_t g0 = range_begin(w, total, G), g1 = range_begin(w + 1, total, G);
 

@@ -104,7 +104,8 @@ def test_decode_append_rejects_bad_arguments(over, status, partitions):
 
 def test_workspace_sizing():
     def ws(workers, D=128):
-        return -(-(4 + 2 * workers) * 4 // 256) * 256 + workers * 2 * (D + 2) * 4
+        # plan: a 4-word header and 3 words per worker, then two fragments per worker
+        return -(-(4 + 3 * workers) * 4 // 256) * 256 + workers * 2 * (D + 2) * 4
     assert pa.decode_workspace_bytes(64, 40, 128, 2048, 16, 300) == ws(300)
     assert pa.decode_workspace_bytes(3, 2, 64, 100, 16, 7) == ws(7, 64)
     assert pa.decode_workspace_bytes(0, 2, 64, 100, 16) == 0
