@@ -296,42 +296,86 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_shared_pas
   if (what & kPassOwn) partition_worker<T, D, B, false, kSharedOwnDepth>(a, w);
 }
 
-// out[s][h] for member j of group g: the pieces of the (g, h) prefix pair and
-// the pass's partial of s's own positions, rescaled to a common max.  One
-// wave per (group, member, head); lane l holds dimensions l, l+64, ...  The
-// work is a few small reads, so their latency is what counts.  The first kU
-// piece slots depend only on (g, j, h), so they are loaded together with the
-// prefix plan before the member ids (and used only for the pieces the plan
-// says exist), and the member's own row right after them: two round trips to
-// memory in the usual case of at most kU pieces.  The sums run over the
-// suffix and then the pieces in order, whichever loop a piece's loads are in.
+// Members one combine wave merges: j and j + kM/2 of its (group, head), so
+// that a launch for the widest groups fits the chip's resident waves at once.
+constexpr int kCombineMembers = 2;
+
+// out[s][h] for members j and j + kM/2 of group g: the pieces of the (g, h)
+// prefix pair and the pass's partial of s's own positions, rescaled to a
+// common max.  One wave per (group, member pair, head); lane l holds
+// dimensions l, l+64, ...  The work is a few small reads, so their latency is
+// what counts.  The first kU piece slots of both members depend only on (g,
+// j, h), so they are loaded together with the prefix plan and the member ids
+// (and used only for the pieces the plan says exist), and the members' own
+// rows right after them: two round trips to memory in the usual case of at
+// most kU pieces.  The sums run over the suffix and then the pieces in order,
+// whichever loop a piece's loads are in.
 template <Dt T, int D>
 __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_combine_kernel(SharedArgs a) {
   constexpr int kM = kSharedMaxMembers;
+  constexpr int kJ = kCombineMembers;
+  constexpr int kSpan = kM / kJ;          // member j + kSpan is the wave's second
   constexpr int kU = 4;                   // pieces loaded up front (and per later batch)
   constexpr int kPer = D / kWave;         // dimensions per lane
   static_assert(D % kWave == 0, "head_dim is whole waves");
+  static_assert(kM % kJ == 0, "members split evenly over the waves");
   const int lane = threadIdx.x % kWave;
   const int w = blockIdx.x * kDecodeWavesPerGroup + wave_id_uniform();
   const int H = a.num_heads;
   const int h = w % H;
-  const int j = (w / H) % kM;
-  const int g = w / (H * kM);
+  const int j0 = (w / H) % kSpan;
+  const int g = w / (H * kSpan);
   if (g >= a.num_groups) return;
   const int C = a.chunks;
   const int64_t chunk_stride = (int64_t)H * kM * (D + 2);  // floats from piece slot c to c+1
-  const float *part0 = a.partials + (((int64_t)g * C * H + h) * kM + j) * (D + 2);
   const uint32_t TP = load_uniform(a.pplan, 0), Gp = load_uniform(a.pplan, 1);
   const uint32_t off = load_uniform(a.pplan, kPrefixPlanHeader + 2 * g);
   const uint32_t tg = load_uniform(a.pplan, kPrefixPlanHeader + 2 * g + 1);
-  float mc0[kU], lc0[kU], v0[kU][kPer];
+  const float *part0[kJ];
+  float mc0[kJ][kU], lc0[kJ][kU], v0[kJ][kU][kPer];
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const bool in = u < C;
-    mc0[u] = in ? load_uniform(part0 + u * chunk_stride, D) : -INFINITY;
-    lc0[u] = in ? load_uniform(part0 + u * chunk_stride, D + 1) : 0.f;
+  for (int m = 0; m < kJ; ++m) {
+    part0[m] = a.partials + (((int64_t)g * C * H + h) * kM + j0 + m * kSpan) * (D + 2);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) v0[u][i] = in ? part0[u * chunk_stride + lane + kWave * i] : 0.f;
+    for (int u = 0; u < kU; ++u) {
+      const bool in = u < C;
+      mc0[m][u] = in ? load_uniform(part0[m] + u * chunk_stride, D) : -INFINITY;
+      lc0[m][u] = in ? load_uniform(part0[m] + u * chunk_stride, D + 1) : 0.f;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) v0[m][u][i] = in ? part0[m][u * chunk_stride + lane + kWave * i] : 0.f;
+    }
+  }
+  // Member j exists only inside the leading run of valid ids (as the prefix
+  // pieces count them).
+  int ids[kM];
+#pragma unroll
+  for (int i = 0; i < kM; ++i) ids[i] = load_uniform(a.members, (int64_t)g * kM + i);
+  bool ok[kJ];
+  int sq[kJ];
+#pragma unroll
+  for (int m = 0; m < kJ; ++m) {
+    ok[m] = true;
+#pragma unroll
+    for (int i = 0; i < kM; ++i)
+      if (i <= j0 + m * kSpan && (ids[i] < 0 || ids[i] >= a.num_seqs)) ok[m] = false;
+    sq[m] = ok[m] ? ids[j0 + m * kSpan] : 0;
+  }
+  bool any = false;
+#pragma unroll
+  for (int m = 0; m < kJ; ++m) any |= ok[m];
+  if (!any) return;
+  // The members' own rows (a member that does not exist reads sequence 0's
+  // and is skipped).
+  int n[kJ], raw[kJ];
+  float m_sfx[kJ], sv[kJ][kPer];
+#pragma unroll
+  for (int m = 0; m < kJ; ++m) {
+    const float *sfx = a.suffix + (int64_t)sq[m] * a.suffix_row + (int64_t)h * (D + 2);
+    n[m] = clip_ctx(load_uniform(a.context_lens, sq[m]), a.ctx_cap);
+    raw[m] = load_uniform(a.starts, sq[m]);
+    m_sfx[m] = load_uniform(sfx, D);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) sv[m][i] = sfx[lane + kWave * i];
   }
   // Pieces of the pair: one per worker whose prefix range meets it.
   int np = 0;
@@ -341,84 +385,72 @@ __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_combine_ke
     np = np < C ? np : C;
   }
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    if (u >= np) {
-      mc0[u] = -INFINITY;
-      lc0[u] = 0.f;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) v0[u][i] = 0.f;
-    }
-  }
-  // Member j exists only inside the leading run of valid ids (as the prefix
-  // pieces count them).
-  int ids[kM];
-#pragma unroll
-  for (int i = 0; i < kM; ++i) ids[i] = load_uniform(a.members, (int64_t)g * kM + i);
-#pragma unroll
-  for (int i = 0; i < kM; ++i)
-    if (i <= j && (ids[i] < 0 || ids[i] >= a.num_seqs)) return;
-  const int s = ids[j];
-  const float *sfx = a.suffix + (int64_t)s * a.suffix_row + (int64_t)h * (D + 2);
-  const int n = clip_ctx(load_uniform(a.context_lens, s), a.ctx_cap);
-  const int raw = load_uniform(a.starts, s);
-  const float m_sfx = load_uniform(sfx, D);
-  float sv[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) sv[i] = sfx[lane + kWave * i];
-  const int st = raw < 0 ? 0 : min(raw & ~(kDecodeTile - 1), n);
-  if (st == 0) return;  // no shared prefix for s: the pass wrote its output
-  // The common max over the suffix and every piece, then the sums.
-  float M = m_sfx;
-#pragma unroll
-  for (int u = 0; u < kU; ++u) M = fmaxf(M, mc0[u]);
-  for (int c0 = kU; c0 < np; c0 += kU) {
-    float mc[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) mc[u] = c0 + u < np ? load_uniform(part0 + (c0 + u) * chunk_stride, D) : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) M = fmaxf(M, mc[u]);
-  }
-  const float mu = (M == -INFINITY) ? 0.f : M;
-  const float ws = fast_exp2(m_sfx - mu);  // the suffix partial is normalised: its sum is 1
-  float L = ws, A[kPer];
-  float e0[kU];
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    e0[u] = fast_exp2(mc0[u] - mu);
-    L += lc0[u] * e0[u];
-  }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    A[i] = sv[i] * ws;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) A[i] += v0[u][i] * e0[u];
-  }
-  for (int c0 = kU; c0 < np; c0 += kU) {
-    float mc[kU], lc[kU], v[kU][kPer];
+  for (int m = 0; m < kJ; ++m) {
+    const int st = raw[m] < 0 ? 0 : min(raw[m] & ~(kDecodeTile - 1), n[m]);
+    if (!ok[m] || st == 0) continue;  // no member, or no shared prefix: the pass wrote the output
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const bool in = c0 + u < np;
-      mc[u] = in ? load_uniform(part0 + (c0 + u) * chunk_stride, D) : -INFINITY;
-      lc[u] = in ? load_uniform(part0 + (c0 + u) * chunk_stride, D + 1) : 0.f;
+      if (u >= np) {
+        mc0[m][u] = -INFINITY;
+        lc0[m][u] = 0.f;
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) v[u][i] = in ? part0[(c0 + u) * chunk_stride + lane + kWave * i] : 0.f;
+        for (int i = 0; i < kPer; ++i) v0[m][u][i] = 0.f;
+      }
     }
+    // The common max over the suffix and every piece, then the sums.
+    float M = m_sfx[m];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) M = fmaxf(M, mc0[m][u]);
+    for (int c0 = kU; c0 < np; c0 += kU) {
+      float mc[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        mc[u] = c0 + u < np ? load_uniform(part0[m] + (c0 + u) * chunk_stride, D) : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) M = fmaxf(M, mc[u]);
+    }
+    const float mu = (M == -INFINITY) ? 0.f : M;
+    const float ws = fast_exp2(m_sfx[m] - mu);  // the suffix partial is normalised: its sum is 1
+    float L = ws, A[kPer];
+    float e0[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const float e = fast_exp2(mc[u] - mu);
-      L += lc[u] * e;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) A[i] += v[u][i] * e;
+      e0[u] = fast_exp2(mc0[m][u] - mu);
+      L += lc0[m][u] * e0[u];
     }
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const float o = A[i] * inv;
-    const int64_t idx = ((int64_t)s * H + h) * D + lane + kWave * i;
-    if constexpr (T == Dt::F32) reinterpret_cast<float *>(a.out)[idx] = o;
-    else if constexpr (T == Dt::F16) reinterpret_cast<uint16_t *>(a.out)[idx] = (uint16_t)f32_to_f16_bits(o);
-    else reinterpret_cast<uint16_t *>(a.out)[idx] = (uint16_t)f32_to_bf16_bits(o);
+    for (int i = 0; i < kPer; ++i) {
+      A[i] = sv[m][i] * ws;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) A[i] += v0[m][u][i] * e0[u];
+    }
+    for (int c0 = kU; c0 < np; c0 += kU) {
+      float mc[kU], lc[kU], v[kU][kPer];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const bool in = c0 + u < np;
+        mc[u] = in ? load_uniform(part0[m] + (c0 + u) * chunk_stride, D) : -INFINITY;
+        lc[u] = in ? load_uniform(part0[m] + (c0 + u) * chunk_stride, D + 1) : 0.f;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) v[u][i] = in ? part0[m][(c0 + u) * chunk_stride + lane + kWave * i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const float e = fast_exp2(mc[u] - mu);
+        L += lc[u] * e;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) A[i] += v[u][i] * e;
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const float o = A[i] * inv;
+      const int64_t idx = ((int64_t)sq[m] * H + h) * D + lane + kWave * i;
+      if constexpr (T == Dt::F32) reinterpret_cast<float *>(a.out)[idx] = o;
+      else if constexpr (T == Dt::F16) reinterpret_cast<uint16_t *>(a.out)[idx] = (uint16_t)f32_to_f16_bits(o);
+      else reinterpret_cast<uint16_t *>(a.out)[idx] = (uint16_t)f32_to_bf16_bits(o);
+    }
   }
 }
 
@@ -479,7 +511,7 @@ hipError_t launch_pass_t(const DecodeArgs &a, const SharedArgs &s, int D, int B,
 
 template <Dt T>
 hipError_t launch_combine_t(const SharedArgs &a, int D, hipStream_t st) {
-  const int64_t items = (int64_t)a.num_groups * kSharedMaxMembers * a.num_heads;
+  const int64_t items = (int64_t)a.num_groups * (kSharedMaxMembers / kCombineMembers) * a.num_heads;
   const dim3 grid((unsigned)((items + kDecodeWavesPerGroup - 1) / kDecodeWavesPerGroup));
   const dim3 block(kDecodeWavesPerGroup * kWave);
   if (D == 64) hipLaunchKernelGGL((decode_combine_kernel<T, 64>), grid, block, 0, st, a);
