@@ -178,3 +178,16 @@ def test_shared_decode_above_the_self_planned_batch():
     out, gp = run_shared(q, k, v, tables, lens, groups, 16, "f16")
     assert (gp == 48).all()
     check_attention(out, ref, "f16", f"{len(lens)} sequences")
+
+
+def test_no_groups_and_groups_without_shared_tiles():
+    """No group at all, then groups whose prompts fill no whole tile: the
+    prefix stream is empty, and every output comes from the own positions."""
+    q, k, v, tables, lens, _ = build("f16", 128, 16, [(5, [3, 9]), (12, [0, 4, 1])], singles=[30, 1], seed=21)
+    ref = oracle.decode(q, k, v, tables, lens, D_SCALE[128], "f16")
+    out, gp = run_shared(q, k, v, tables, lens, [], 16, "f16")
+    assert gp.size == 0
+    check_attention(out, ref, "f16", "no groups")
+    out, gp = run_shared(q, k, v, tables, lens, [[0, 1], [2, 3, 4]], 16, "f16")
+    assert gp.size == 2 and (gp == 0).all()
+    check_attention(out, ref, "f16", "groups without a shared tile")
