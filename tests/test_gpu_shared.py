@@ -191,3 +191,25 @@ def test_no_groups_and_groups_without_shared_tiles():
     out, gp = run_shared(q, k, v, tables, lens, [[0, 1], [2, 3, 4]], 16, "f16")
     assert gp.size == 2 and (gp == 0).all()
     check_attention(out, ref, "f16", "groups without a shared tile")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shared_decode(seed):
+    """Seeded random layouts: prompts of any length, 1 to 11 members with
+    tails of 0 to 80 tokens, sequences in no group, any dtype, head_dim and
+    block size, and a random worker count (the prefix split and the own
+    positions' split change with it)."""
+    rng = np.random.default_rng(4000 + seed)
+    dtype = str(rng.choice(W.DTYPES))
+    D = int(rng.choice([64, 128]))
+    B = int(rng.choice([16, 32, 64]))
+    spec = [(int(rng.integers(1, 400)), [int(t) for t in rng.integers(0, 81, size=int(rng.integers(1, 12)))])
+            for _ in range(int(rng.integers(1, 9)))]
+    singles = [int(n) for n in rng.integers(1, 300, size=int(rng.integers(0, 4)))]
+    H = int(rng.integers(1, 5))
+    q, k, v, tables, lens, groups = build(dtype, D, B, spec, singles=singles, seed=seed, H=H)
+    workers = int(rng.choice([0, 1, 2, 5, 33, 500]))
+    say(f"  seed {seed}: {dtype} D={D} B={B} H={H} workers={workers} spec={spec} singles={singles}")
+    ref = oracle.decode(q, k, v, tables, lens, D_SCALE[D], dtype)
+    out, gp = run_shared(q, k, v, tables, lens, groups, B, dtype, workers)
+    check_attention(out, ref, dtype, f"random shared decode seed {seed}")
