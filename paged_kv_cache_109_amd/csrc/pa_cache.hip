@@ -123,27 +123,39 @@ struct LayerPtrs {
   char *v[kCopyMaxLayers];
 };
 
-constexpr int kCopyUnroll = 4;
-constexpr int64_t kCopyChunk = (int64_t)kCacheThreads * 16 * kCopyUnroll;  // bytes per workgroup
+// 16-byte chunks per lane: a copy-on-write copy within the pool, and a swap
+// between two pools (whose other side is reached over the host link, so it
+// keeps more requests in flight per lane).
+constexpr int kCopyUnroll = 2;
+constexpr int kSwapUnroll = 4;
+template <int kUnroll>
+constexpr int64_t chunk_bytes() { return (int64_t)kCacheThreads * 16 * kUnroll; }  // bytes per workgroup
 
-// One workgroup's part of a whole-block copy: chunk `chunk` (kCopyChunk
-// bytes) of the block_bytes at `from` onto `to`.  Each lane has all its
-// loads in flight before its first store.  Shared by the copy-on-write copy
-// within a pool and the swap between two pools.
+// One workgroup's part of a whole-block copy: chunk `chunk` (kUnroll * 4 KB)
+// of the block_bytes at `from` onto `to`.  Each lane has all its loads in
+// flight before its first store.  kStreamStores: the stores are
+// non-temporal, so the copied blocks do not push out of the caches the
+// blocks that are read again next -- the source block, which the copies of
+// several forks read in turn, and the shared prompt blocks the decode that
+// follows reads once per sample.
+template <int kUnroll, bool kStreamStores>
 __device__ __forceinline__ void copy_block_chunk(const char *from, char *to, int64_t block_bytes, int64_t chunk) {
-  const int64_t begin = chunk * kCopyChunk;
-  uint4 r[kCopyUnroll];
-  bool live[kCopyUnroll];
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const int64_t begin = chunk * chunk_bytes<kUnroll>();
+  u32x4 r[kUnroll];
+  bool live[kUnroll];
 #pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
+  for (int u = 0; u < kUnroll; ++u) {
     const int64_t o = begin + ((int64_t)u * kCacheThreads + threadIdx.x) * 16;
     live[u] = o < block_bytes;
-    if (live[u]) r[u] = *reinterpret_cast<const uint4 *>(from + o);
+    if (live[u]) r[u] = *reinterpret_cast<const u32x4 *>(from + o);
   }
 #pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
+  for (int u = 0; u < kUnroll; ++u) {
     const int64_t o = begin + ((int64_t)u * kCacheThreads + threadIdx.x) * 16;
-    if (live[u]) *reinterpret_cast<uint4 *>(to + o) = r[u];
+    if (!live[u]) continue;
+    if constexpr (kStreamStores) __builtin_nontemporal_store(r[u], reinterpret_cast<u32x4 *>(to + o));
+    else *reinterpret_cast<u32x4 *>(to + o) = r[u];
   }
 }
 
@@ -159,13 +171,13 @@ __global__ __launch_bounds__(kCacheThreads) void copy_blocks_kernel(LayerPtrs pt
   const int64_t src = mapping[2 * pair];
   const int64_t dst = mapping[2 * pair + 1];
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  copy_block_chunk(base + src * block_bytes, base + dst * block_bytes, block_bytes, chunk);
+  copy_block_chunk<kCopyUnroll, true>(base + src * block_bytes, base + dst * block_bytes, block_bytes, chunk);
 }
 
 hipError_t launch_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t num_layers,
                               const int64_t *block_mapping, int64_t num_pairs, int64_t block_bytes,
                               int64_t num_blocks, hipStream_t stream) {
-  const int64_t chunks = (block_bytes + kCopyChunk - 1) / kCopyChunk;
+  const int64_t chunks = (block_bytes + chunk_bytes<kCopyUnroll>() - 1) / chunk_bytes<kCopyUnroll>();
   const int64_t max_pairs = 0x7fffffff / chunks;
   for (int32_t l0 = 0; l0 < num_layers; l0 += kCopyMaxLayers) {
     const int32_t nl = num_layers - l0 < kCopyMaxLayers ? num_layers - l0 : kCopyMaxLayers;
@@ -208,14 +220,14 @@ __global__ __launch_bounds__(kCacheThreads) void swap_blocks_kernel(SwapPtrs ptr
   const int64_t src = mapping[2 * pair];
   const int64_t dst = mapping[2 * pair + 1];
   if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
-  copy_block_chunk(ptrs.src[blockIdx.y] + src * block_bytes, ptrs.dst[blockIdx.y] + dst * block_bytes, block_bytes,
-                   chunk);
+  copy_block_chunk<kSwapUnroll, false>(ptrs.src[blockIdx.y] + src * block_bytes,
+                                       ptrs.dst[blockIdx.y] + dst * block_bytes, block_bytes, chunk);
 }
 
 hipError_t launch_swap_blocks(const void *const *src_caches, void *const *dst_caches, int32_t num_caches,
                               const int64_t *block_mapping, int64_t num_pairs, int64_t block_bytes,
                               int64_t src_blocks, int64_t dst_blocks, hipStream_t stream) {
-  const int64_t chunks = (block_bytes + kCopyChunk - 1) / kCopyChunk;
+  const int64_t chunks = (block_bytes + chunk_bytes<kSwapUnroll>() - 1) / chunk_bytes<kSwapUnroll>();
   const int64_t max_pairs = 0x7fffffff / chunks;
   for (int32_t c0 = 0; c0 < num_caches; c0 += kSwapMaxCaches) {
     const int32_t nc = num_caches - c0 < kSwapMaxCaches ? num_caches - c0 : kSwapMaxCaches;
