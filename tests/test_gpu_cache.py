@@ -41,16 +41,19 @@ def test_reshape_and_cache_skips_out_of_pool_slots():
     assert int((k != 0).sum()) == 2 * 64 and bool((k[0, :, 5] == 1).all())
 
 
-@pytest.mark.parametrize("layers", [1, 3, 70])
-def test_copy_blocks_bit_exact(layers):
+@pytest.mark.parametrize("layers,shape", [(1, (24, 3, 16, 64)), (3, (24, 3, 16, 64)), (70, (24, 3, 16, 64)),
+                                          (2, (12, 5, 16, 128)), (1, (16, 40, 16, 128))])
+def test_copy_blocks_bit_exact(layers, shape):
+    # Blocks of 6 KB (less than one workgroup's 8 KB chunk), 20 KB (two chunks
+    # and a partial third) and 160 KB (OPT-13B: twenty whole chunks).
     rng = np.random.default_rng(layers)
-    N, H, B, D = 24, 3, 16, 64
+    N, H, B, D = shape
     ks = [W.cast(rng.standard_normal((N, H, B, D), dtype=np.float32), "bf16") for _ in range(layers)]
     vs = [W.cast(rng.standard_normal((N, H, B, D), dtype=np.float32), "bf16") for _ in range(layers)]
-    pairs = np.array([[2, 9], [2, 10], [2, 11], [5, 0], [17, 23], [4, 13]], np.int64)
+    pairs = np.array([[2, 9], [2, 10], [2, 11], [5, 0], [7, 8], [4, 3]], np.int64)
     kd = [dev(a, "bf16") for a in ks]
     vd = [dev(a, "bf16") for a in vs]
-    say(f"  copy_blocks layers={layers} pairs={len(pairs)}")
+    say(f"  copy_blocks layers={layers} shape={shape} pairs={len(pairs)}")
     pa.copy_blocks(kd, vd, dev(pairs))
     torch.cuda.synchronize()
     oracle.copy_blocks(ks, vs, pairs)
