@@ -498,6 +498,35 @@ def run_decode(name, args, stream_read, cpu_seconds):
               f"decode call {dec_s * 1e6:.1f} us, {distinct / dec_s / 1e9:.0f} GB/s of distinct blocks",
               file=sys.stderr, flush=True)
 
+        # The same plain step told that the sequences share blocks
+        # (pa_paged_attention_decode_ex, PA_DECODE_REUSED_BLOCKS): ordinary
+        # K/V loads, so the caches can serve the samples' repeated reads.
+        def reused_step(i, ev=None):
+            k_cache, v_cache = pools[i % len(pools)]
+            pa.copy_blocks([k_cache], [v_cache], mapping)
+            if ev is not None:
+                ev[0].record(stream)
+            pa.paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_ctx, case.scale,
+                                      workspace=ws, split_workers=workers, reused_blocks=True)
+            if ev is not None:
+                ev[1].record(stream)
+
+        for i in range(args.warmup):
+            reused_step(i)
+        ru_ms, _ = timed_steps(torch, reused_step, args, len(pools))
+        rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):
+            reused_step(i, rev[i])
+        torch.cuda.synchronize()
+        ru_calls = [a.elapsed_time(z) for a, z in rev]
+        ru_s = float(np.mean(ru_calls)) * 1e-3
+        components["decode_reused_blocks"] = {
+            "step_us": ru_ms * 1e3, "tokens_per_s": S / (ru_ms * 1e-3), "decode_call_avg_us": ru_s * 1e6,
+            **launch_stats(ru_calls), "logical_kv_gbps": kv_bytes / ru_s / 1e9}
+        print(f"[bench] plain decode with reused blocks: step {ru_ms * 1e3:.1f} us ({S / (ru_ms * 1e-3):.0f} "
+              f"tokens/s); decode call {ru_s * 1e6:.1f} us, {kv_bytes / ru_s / 1e9:.0f} GB/s of logical K/V",
+              file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle

@@ -172,7 +172,7 @@ int32_t pa_decode_default_workers(pa_dtype dtype, int32_t head_dim, int32_t bloc
 
 /* Workspace bytes pa_paged_attention_decode needs for up to split_workers
  * worker waves (0: an upper bound for the current device); 0 only for
- * num_seqs 0.  Layout: the work plan (uint32: 4 header words plus two per
+ * num_seqs 0.  Layout: the work plan (uint32: 4 header words plus three per
  * worker, padded to 256 bytes), then two fp32 partial results of head_dim + 2
  * floats per worker.  Its contents need no initialisation; calls that share
  * one workspace must be ordered on one stream. */
@@ -206,6 +206,35 @@ pa_status pa_paged_attention_decode(void *out, const void *q, const void *k_cach
                                     int32_t head_dim, int32_t block_size, int64_t num_blocks,
                                     float scale, pa_dtype dtype, int32_t split_workers,
                                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pa_paged_attention_decode_ex -- pa_paged_attention_decode with flags that
+ * choose how the kernels read the cache; the output bytes do not depend on
+ * them.
+ *
+ * PA_DECODE_REUSED_BLOCKS: the batch's sequences point at some of the same
+ * physical blocks (samples forked from one prompt, beams of one search:
+ * paper notes "PagedAttention: Efficient Memory Management for Large
+ * Language Model Serving", sections 3.4.1 Parallel sampling and 3.4.2 Beam
+ * search), so a block is read once per sequence that holds it.  K/V are then read with ordinary loads, which leave them in
+ * the caches for the next reader; without the flag they are read with
+ * non-temporal loads, the faster choice when every block is read once.  When
+ * the sharing is a common prompt prefix of known groups,
+ * pa_paged_attention_decode_shared reads each shared block only once.
+ *
+ *  flags  0 or PA_DECODE_REUSED_BLOCKS; any other bit gives
+ *         PA_ERR_INVALID_ARG.  All other arguments, the workspace and the
+ *         result are as for pa_paged_attention_decode.
+ */
+#define PA_DECODE_REUSED_BLOCKS 1u
+pa_status pa_paged_attention_decode_ex(void *out, const void *q, const void *k_cache,
+                                       const void *v_cache, const int32_t *block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                       int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                                       int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                       float scale, pa_dtype dtype, int32_t split_workers,
+                                       uint32_t flags, void *workspace, size_t workspace_bytes,
+                                       void *stream);
 
 /*
  * pa_paged_attention_decode_noalloc -- pa_paged_attention_decode without a

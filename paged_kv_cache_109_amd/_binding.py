@@ -37,6 +37,9 @@ _SIGS = {
     "pa_decode_workspace_bytes": ([i32, i32, i32, i32, i32, i32], sz),
     "pa_paged_attention_decode": (
         [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, i32, P, sz, P], ctypes.c_int),
+    "pa_paged_attention_decode_ex": (
+        [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, i32, ctypes.c_uint32, P, sz, P],
+        ctypes.c_int),
     "pa_paged_attention_decode_noalloc": (
         [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int, i32, P], ctypes.c_int),
     "pa_paged_attention_decode_partitions": (
@@ -212,19 +215,29 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_conte
             _pa_dtype(q), int(split_workers), ws_ptr, ws_bytes, _stream(stream))
 
 
+DECODE_REUSED_BLOCKS = 1  # PA_DECODE_REUSED_BLOCKS
+
+
 def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
                            scale: float, workspace: Optional[torch.Tensor] = None, split_workers: int = 0,
-                           stream=None) -> torch.Tensor:
+                           stream=None, reused_blocks: bool = False) -> torch.Tensor:
     """out[s, h] = softmax(scale * q[s, h] . K) V over the first context_lens[s]
     positions of sequence s, read through block_tables. Allocates the
-    workspace with torch when none is given."""
+    workspace with torch when none is given. reused_blocks: the sequences
+    share physical blocks (forked samples, beams), so K/V are read with
+    ordinary loads the caches can serve again (pa_paged_attention_decode_ex);
+    the output is the same."""
     if workspace is None:
         workspace = alloc_decode_workspace(q.shape[0], k_cache.shape[1], k_cache.shape[3], max_context_len,
                                            k_cache.shape[2], split_workers, device=q.device)
-    _check(_lib.pa_paged_attention_decode(*_decode_args(out, q, k_cache, v_cache, block_tables, context_lens,
-                                                        max_context_len, scale, split_workers, workspace,
-                                                        stream)), "paged_attention_decode")
+    args = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale, split_workers,
+                        workspace, stream)
+    if reused_blocks:
+        _check(_lib.pa_paged_attention_decode_ex(*args[:16], DECODE_REUSED_BLOCKS, *args[16:]),
+               "paged_attention_decode_ex")
+    else:
+        _check(_lib.pa_paged_attention_decode(*args), "paged_attention_decode")
     return out
 
 

@@ -157,6 +157,7 @@ pa::DecodeArgs decode_args(void *out, const void *q, const void *k_cache, const 
   a.workers = (int32_t)g.workers;
   a.out_row_words = (int32_t)((int64_t)num_heads * head_dim * elt_bytes(dtype) / 4);
   a.scale_log2 = scale * kLog2e;
+  a.reused_blocks = 0;
   a.starts = nullptr;
   a.suffix_out = nullptr;
   a.suffix_row = num_heads * (head_dim + 2);
@@ -333,7 +334,8 @@ static pa_status decode_impl(bool run_parts, bool run_reduce, void *out, const v
                              const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
                              int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                              float scale, pa_dtype dtype, int32_t split_workers, void *workspace,
-                             size_t workspace_bytes, void *stream, const AppendRows *app = nullptr) {
+                             size_t workspace_bytes, void *stream, const AppendRows *app = nullptr,
+                             bool reused_blocks = false) {
   pa_status st = check_decode_common(k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                                      max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks,
                                      dtype, split_workers);
@@ -359,6 +361,7 @@ static pa_status decode_impl(bool run_parts, bool run_reduce, void *out, const v
   if (st != PA_OK) return st;
   pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                                  num_seqs, num_heads, head_dim, block_size, dtype, num_blocks, scale, g, workspace);
+  a.reused_blocks = reused_blocks ? 1 : 0;
   if (app) {
     a.new_key = app->key;
     a.new_value = app->value;
@@ -391,6 +394,20 @@ pa_status pa_paged_attention_decode(void *out, const void *q, const void *k_cach
   return decode_impl(true, true, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                      max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks, scale, dtype,
                      split_workers, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_paged_attention_decode_ex(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                       const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                                       int32_t num_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                       float scale, pa_dtype dtype, int32_t split_workers, uint32_t flags,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+  if (flags & ~(uint32_t)PA_DECODE_REUSED_BLOCKS)
+    return fail(PA_ERR_INVALID_ARG, "unknown decode flags 0x%x", flags & ~(uint32_t)PA_DECODE_REUSED_BLOCKS);
+  return decode_impl(true, true, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, num_seqs, num_heads, head_dim, block_size, num_blocks, scale, dtype,
+                     split_workers, workspace, workspace_bytes, stream, nullptr,
+                     (flags & PA_DECODE_REUSED_BLOCKS) != 0);
 }
 
 pa_status pa_paged_attention_decode_noalloc(void *out, const void *q, const void *k_cache, const void *v_cache,

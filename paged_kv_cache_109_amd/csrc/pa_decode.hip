@@ -180,9 +180,9 @@ __device__ __forceinline__ void merge_fragments(const DecodeArgs &a, uint32_t wa
 }
 
 // The partition pass: every wave of the grid is one stream-K worker.
-template <Dt T, int D, int B, bool kAppend>
+template <Dt T, int D, int B, bool kAppend, bool kStream = kStreamLoads>
 __global__ __launch_bounds__(kDecodeWavesPerGroup *kWave) void decode_partition_kernel(DecodeArgs a) {
-  partition_worker<T, D, B, kAppend, kDepth>(a, blockIdx.x * kDecodeWavesPerGroup + wave_id_uniform());
+  partition_worker<T, D, B, kAppend, kDepth, kStream>(a, blockIdx.x * kDecodeWavesPerGroup + wave_id_uniform());
 }
 
 // Merge the fragments of every pair cut by range boundaries.  Worker wave w
@@ -285,6 +285,9 @@ static hipError_t launch_part(const DecodeArgs &a, hipStream_t st) {
   if (a.new_key)
     hipLaunchKernelGGL((decode_partition_kernel<T, D, B, true>), dim3(groups), dim3(kDecodeWavesPerGroup * kWave), 0,
                        st, a);
+  else if (a.reused_blocks)
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, B, false, false>), dim3(groups),
+                       dim3(kDecodeWavesPerGroup * kWave), 0, st, a);
   else
     hipLaunchKernelGGL((decode_partition_kernel<T, D, B, false>), dim3(groups), dim3(kDecodeWavesPerGroup * kWave), 0,
                        st, a);

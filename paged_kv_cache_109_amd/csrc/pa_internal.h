@@ -34,6 +34,7 @@ struct DecodeArgs {
   int32_t workers;        // worker waves launched (the split of the tile stream)
   int32_t out_row_words;  // 32-bit words of one sequence's output rows (H*D*elt/4)
   float scale_log2;       // softmax scale * log2(e)
+  int32_t reused_blocks;  // nonzero: the sequences share K/V blocks, read them with ordinary loads
   // Shared-prefix decode only (both null otherwise): starts[s] is the first
   // position the pass covers for sequence s (a multiple of kDecodeTile);
   // for s with starts[s] > 0 the pass leaves fp32 partials in suffix_out

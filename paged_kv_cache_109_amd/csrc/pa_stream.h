@@ -13,7 +13,7 @@
 #ifndef PA_DECODE_DEPTH
 #define PA_DECODE_DEPTH 3
 #endif
-// 1: stream K/V with non-temporal loads (they are read exactly once).
+// 1: by default, stream K/V with non-temporal loads (each is read once).
 #ifndef PA_DECODE_NT
 #define PA_DECODE_NT 1
 #endif
@@ -21,15 +21,17 @@
 namespace pa {
 
 constexpr int kDepth = PA_DECODE_DEPTH;
+constexpr bool kStreamLoads = PA_DECODE_NT != 0;
 // Largest batch whose worker waves plan for themselves (16 chunks of 64).
 constexpr int kSelfPlanSeqs = 1024;
 
-__device__ __forceinline__ uint4 load16(const char *p) {
-#if PA_DECODE_NT
-  return load_nt16(p);
-#else
-  return *reinterpret_cast<const uint4 *>(p);
-#endif
+// A 16-byte K/V load: non-temporal when every block is read once
+// (kStream), ordinary when the batch's sequences share blocks, so that the
+// caches can serve the repeated reads.
+template <bool kStream>
+__device__ __forceinline__ uint4 load_kv16(const char *p) {
+  if constexpr (kStream) return load_nt16(p);
+  else return *reinterpret_cast<const uint4 *>(p);
 }
 
 __device__ __forceinline__ int clip_ctx(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
@@ -212,8 +214,9 @@ __device__ __forceinline__ uint32_t first_worker(uint32_t pair_start, uint32_t t
 // One worker wave's share of the partition pass.  kAppend: each sequence's
 // newest token (position n - 1) is read from a.new_key / a.new_value instead
 // of the cache.  The pass only reads; the rows are stored into the cache by
-// the reduce pass, after every read of this launch.
-template <Dt T, int D, int B, bool kAppend, int kDepthT>
+// the reduce pass, after every read of this launch.  kStream: the K/V loads
+// are non-temporal (see load_kv16).
+template <Dt T, int D, int B, bool kAppend, int kDepthT, bool kStream = kStreamLoads>
 __device__ __forceinline__ void partition_worker(const DecodeArgs &a, uint32_t w) {
   using R = RowShape<T, D, kDecodeTile>;
   const int lane = threadIdx.x % kWave;
@@ -294,11 +297,11 @@ __device__ __forceinline__ void partition_worker(const DecodeArgs &a, uint32_t w
           vp = reinterpret_cast<const char *>(a.new_value) + (int64_t)s * a.new_value_stride + h * R::kRowBytes +
                col * 16;
         }
-        kf[i] = load16(kp);
-        vf[i] = load16(vp);
+        kf[i] = load_kv16<kStream>(kp);
+        vf[i] = load_kv16<kStream>(vp);
       } else {
-        kf[i] = load16(kbase + off);
-        vf[i] = load16(vbase + off);
+        kf[i] = load_kv16<kStream>(kbase + off);
+        vf[i] = load_kv16<kStream>(vbase + off);
       }
       okm |= ok ? (1u << i) : 0u;
     }

@@ -68,6 +68,22 @@ def test_decode_rejects_bad_arguments(over, status):
     assert B._lib.pa_last_error()
 
 
+@pytest.mark.parametrize("over,flags,status", [
+    ({}, 2, 1), ({}, 0x80000000, 1), ({}, 3, 1), (dict(dt=7), 1, 1), (dict(D=96), 1, 2), (dict(S=70000), 0, 2),
+    (dict(max_ctx=2048, M=128), 1, 3),
+])
+def test_decode_ex_rejects_bad_arguments(over, flags, status):
+    # Unknown flag bits are refused; otherwise the checks are the plain decode's.
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, M=8, ctx=FAKE, max_ctx=100, S=2, H=4, D=128, Bs=16, N=64,
+             scale=0.1, dt=1, part=0, ws=None, ws_bytes=0, stream=None)
+    a.update(over)
+    got = B._lib.pa_paged_attention_decode_ex(a["out"], a["q"], a["k"], a["v"], a["bt"], a["M"], a["ctx"],
+                                              a["max_ctx"], a["S"], a["H"], a["D"], a["Bs"], a["N"], a["scale"],
+                                              a["dt"], a["part"], flags, a["ws"], a["ws_bytes"], a["stream"])
+    assert got == status
+    assert B._lib.pa_last_error()
+
+
 @pytest.mark.parametrize("over,status", [
     (dict(dt=7), 1), (dict(H=0), 1), (dict(D=96), 2), (dict(k=None), 1), (dict(part=-1), 1), (dict(S=70000), 2),
 ])

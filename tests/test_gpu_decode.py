@@ -201,3 +201,38 @@ def test_long_contexts(dtype, B):
     c = W.make_decode_case(len(lens), 2, 128, B, dtype, lens, seed=5, max_blocks_per_seq=W.blocks_needed(50001, B))
     dc = DeviceCase(c)
     check_attention(gpu_decode(dc), ref_decode(c), dtype, f"long contexts {dtype} B={B}")
+
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+@pytest.mark.parametrize("D,B", [(64, 4), (128, 16), (128, 32)])
+def test_reused_blocks_flag_gives_the_same_bytes(dtype, D, B):
+    """The flag only changes how K/V are loaded (ordinary instead of
+    non-temporal loads): the output bytes equal the plain call's, at the
+    default split and at a few others, and the oracle's within tolerance."""
+    c = W.make_decode_case(len(LENS), 3, D, B, dtype, LENS, seed=7 * B + D, extra_blocks=5,
+                           max_blocks_per_seq=W.blocks_needed(max(LENS), B) + 2, poison_unused=True, pad_entry=-1)
+    dc = DeviceCase(c)
+    ref = ref_decode(c)
+    for workers in (0, 1, 97):
+        plain = gpu_decode(dc, workers).clone()
+        say(f"  decode_ex reused_blocks {c.name} workers={workers}")
+        pa.paged_attention_decode(dc.out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
+                                  c.max_context_len, c.scale, split_workers=workers, reused_blocks=True)
+        torch.cuda.synchronize()
+        assert torch.equal(dc.out.view(torch.uint8), plain.view(torch.uint8))
+        check_attention(dc.out, ref, dtype, f"{c.name} reused_blocks workers={workers}")
+
+
+def test_reused_blocks_flag_on_forked_samples_full_size():
+    """The workload the flag is for: 192 samples forked from 32 prompts,
+    which share their prompts' blocks. Same bytes as the plain call."""
+    c = W.parallel_sampling()
+    dc = DeviceCase(c)
+    pa.copy_blocks([dc.k_cache], [dc.v_cache], torch.from_numpy(c.block_mapping).cuda())  # the forks' copy-on-write
+    plain = gpu_decode(dc).clone()
+    assert torch.isfinite(plain).all()
+    say(f"  decode_ex reused_blocks {c.name}")
+    pa.paged_attention_decode(dc.out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
+                              c.max_context_len, c.scale, reused_blocks=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dc.out.view(torch.uint8), plain.view(torch.uint8))
