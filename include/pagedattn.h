@@ -216,11 +216,12 @@ pa_status pa_paged_attention_decode(void *out, const void *q, const void *k_cach
  * physical blocks (samples forked from one prompt, beams of one search:
  * paper notes "PagedAttention: Efficient Memory Management for Large
  * Language Model Serving", sections 3.4.1 Parallel sampling and 3.4.2 Beam
- * search), so a block is read once per sequence that holds it.  K/V are then read with ordinary loads, which leave them in
- * the caches for the next reader; without the flag they are read with
- * non-temporal loads, the faster choice when every block is read once.  When
- * the sharing is a common prompt prefix of known groups,
- * pa_paged_attention_decode_shared reads each shared block only once.
+ * search), so a block is read once per sequence that holds it.  K/V are
+ * then read with ordinary loads, which leave them in the caches for the next
+ * reader; without the flag they are read with non-temporal loads, the faster
+ * choice when every block is read once.  When the sharing is a common prompt
+ * prefix of known groups, pa_paged_attention_decode_shared reads each shared
+ * block only once.
  *
  *  flags  0 or PA_DECODE_REUSED_BLOCKS; any other bit gives
  *         PA_ERR_INVALID_ARG.  All other arguments, the workspace and the
