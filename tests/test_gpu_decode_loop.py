@@ -114,9 +114,14 @@ def test_decode_loop_with_forks_copy_on_write_and_frees(dtype):
         out = torch.empty((len(live), H, D), dtype=tdt, device="cuda")
         say(f"  {dtype} step {step}: {len(live)} sequences, lengths {lens.tolist()}, {len(copies)} copies, "
             f"{bm.num_free()} blocks free")
-        pa.paged_attention_decode(out, dev(q, dtype), k_cache, v_cache, dev(tables), dev(lens), int(lens.max()),
-                                  scale)
+        qd, td, ld = dev(q, dtype), dev(tables), dev(lens)
+        pa.paged_attention_decode(out, qd, k_cache, v_cache, td, ld, int(lens.max()), scale)
         torch.cuda.synchronize()
         want = reference(q, [hist[s] for s in live], scale, dtype)
         check_attention(out, want, dtype, f"{dtype} step {step}")
+        # The forks share blocks: the reused-blocks load policy gives the same bytes.
+        out2 = torch.empty_like(out)
+        pa.paged_attention_decode(out2, qd, k_cache, v_cache, td, ld, int(lens.max()), scale, reused_blocks=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out2.view(torch.uint8), out.view(torch.uint8)), f"{dtype} step {step}: reused_blocks"
     assert copies_seen >= 3
